@@ -1,0 +1,365 @@
+/*
+ * mxq_oracle.c -- plain, slow, obviously-correct CPU oracle for OCP MXFP4
+ * and NVFP4 microscaling.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path (the HIP library and
+ * its Python binding) may include, link, load or call this file.  Only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark use it.
+ * It shares no header, table, helper or constant with the GPU sources.
+ *
+ * Sources (the web pages the method is described on):
+ *   [EXPLAINER]  "Low-precision inference and MXFP4 quantization"
+ *                (mingyuyang.com AI daily, 2026-08-05), sec. 3 "Core idea:
+ *                block scaling makes 4 bits usable".
+ *   [TRANSFP4]   "Portable FP4 quantization for heterogeneous accelerators"
+ *                (elexvx.com research), sec. 1.1 eq. (1), sec. 3.1, sec. 3.2.
+ *   [GUIDE]      "4.5 FP8 and NVFP4/MXFP4" (infra-guide, inference
+ *                optimization ch. 4), sec. 1.1, 1.2, 2, 3.1, 3.3, 4.1.
+ *   [GPTOSS]     gpt-oss MXFP4 repost (juejin.cn post 7539732578421833769),
+ *                section "MXFP4" with the four-value worked example.
+ *
+ * Precision discipline: every MXFP4 decision is exact (power-of-two scaling
+ * of a float in double, then nearest-value search in double).  NVFP4 works
+ * in IEEE fp32 because its tensor scale is an FP32 number [GUIDE sec. 4.1];
+ * build with -ffp-contract=off and without fast-math so each fp32 operation
+ * rounds once, to nearest even.  Products accumulate in double.
+ *
+ * Readings the pages leave open (each one is listed in the design notes):
+ *   - E2M1 ties: round-to-nearest-even by default; a ties-away mode exists
+ *     only to reproduce the worked example as printed [GPTOSS].
+ *   - E8M0 exponent: e = floor(log2 amax) - 2, clamped to [-127, 127];
+ *     an all-zero block takes e = -127 (scale code 0).
+ *   - Nibble order: element 2j in the low nibble of byte j.
+ *   - NVFP4 tensor scale: s_t = amax_t / (6 * 448) in fp32, stored as the
+ *     dequantization multiplier; s_t = 1 for an all-zero tensor.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+/* ------------------------------------------------------------------ */
+/* Element formats                                                     */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 value of a 4-bit code [GUIDE sec. 3.1]: one sign bit, two exponent
+ * bits, one mantissa bit (S EE M from the most significant bit).  With
+ * exponent bias 1, E = 0 is subnormal with step 0.5, and the largest value
+ * is 2^2 * 1.5 = 6, as the guide states. */
+double or_e2m1_decode(uint8_t code)
+{
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * m;
+    else
+        mag = ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E2M1 encode: the representable magnitude nearest to |v|; magnitudes at or
+ * above the largest value (6) saturate to 6.
+ * An exact tie between two neighbours goes to the code whose mantissa bit is
+ * 0 (round half to even), or, in ties_away mode, to the larger magnitude.
+ * The sign bit copies the sign of v, so -0 and small negatives give 0x8. */
+uint8_t or_e2m1_encode(double v, int ties_away)
+{
+    double a = fabs(v);
+    int best = 0;
+    double bestd = INFINITY;
+    if (a >= 6.0) /* saturate: explicit, so huge |v| never ties in rounding */
+        return (uint8_t)(7 | (signbit(v) ? 8 : 0));
+    for (int c = 0; c < 8; c++) {
+        double d = fabs(a - or_e2m1_decode((uint8_t)c));
+        if (d < bestd) {
+            best = c;
+            bestd = d;
+        } else if (d == bestd) {
+            /* tie between best (smaller magnitude) and c (larger) */
+            if (ties_away)
+                best = c;
+            else if ((c & 1) == 0)
+                best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 8 : 0));
+}
+
+/* E4M3 value of an 8-bit code [GUIDE sec. 1.1-1.2]: S EEEE MMM, bias 7
+ * (bits 00111000 read as 1.0), subnormals for E = 0, no infinities, and the
+ * single all-ones pattern S 1111 111 is NaN, so the largest finite value is
+ * 2^8 * 1.75 = 448. */
+double or_e4m3_decode(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp(m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* E4M3 encode of a non-negative fp32 value: nearest finite E4M3 value,
+ * ties to the code with mantissa LSB 0, saturating at 448 (a real type cast,
+ * not rounding to an integer grid [GUIDE sec. 1.2 key point]).  Negative
+ * inputs encode their magnitude with the sign bit set. */
+uint8_t or_e4m3_encode(float r)
+{
+    double a = fabs((double)r);
+    int best = 0;
+    double bestd = INFINITY;
+    if (a >= 448.0) /* saturate at the largest finite value, never NaN */
+        return (uint8_t)(0x7E | (signbit(r) ? 0x80 : 0));
+    for (int c = 0; c < 0x7F; c++) { /* 0x7F is NaN */
+        double d = fabs(a - or_e4m3_decode((uint8_t)c));
+        if (d < bestd) {
+            best = c;
+            bestd = d;
+        } else if (d == bestd && (c & 1) == 0) {
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(r) ? 0x80 : 0));
+}
+
+/* ------------------------------------------------------------------ */
+/* Input widening (definitions of the storage types)                   */
+/* ------------------------------------------------------------------ */
+
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16; /* bf16 is the top half of an fp32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static float load_elem(const void *x, int dtype, int64_t i)
+{
+    if (dtype == OR_BF16)
+        return bf16_to_f32(((const uint16_t *)x)[i]);
+    return ((const float *)x)[i];
+}
+
+void or_to_f64(const void *x, int dtype, int64_t n, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        y[i] = (double)load_elem(x, dtype, i);
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4                                                               */
+/* ------------------------------------------------------------------ */
+
+/* Shared block exponent.  The block's largest magnitude is mapped near the
+ * largest E2M1 value by a power-of-two scale [EXPLAINER sec. 3; TRANSFP4
+ * sec. 1.1: an E8M0 scale is a pure exponent].  Rule: e = floor(log2 amax)
+ * - 2, clamped to the E8M0 range [-127, 127]; amax = 0 gives -127. */
+int or_e8m0_exponent(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int ex;
+    frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex-1 */
+    int e = (ex - 1) - 2;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+/* E8M0 scale value: 2^(code - 127); code 255 is NaN. */
+double or_e8m0_decode(uint8_t code)
+{
+    if (code == 255)
+        return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* Quantize rows x[rows][k] along k in blocks of 32 [GUIDE sec. 4.1 table:
+ * 32 E2M1 elements share one E8M0 scale].  Eq. (1) of [TRANSFP4] with
+ * s_g = 1: q_i = Q(x_i / s_b).  Outputs: q[rows][k/2] packed nibbles (element
+ * 2j low), s[rows][k/32] E8M0 codes.  k must be a multiple of 32. */
+void or_mx_quantize(const void *x, int dtype, int64_t rows, int64_t k,
+                    uint8_t *q, uint8_t *s, int ties_away)
+{
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            int64_t base = r * k + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; i++) {
+                double a = fabs((double)load_elem(x, dtype, base + i));
+                if (a > amax)
+                    amax = a;
+            }
+            int e = or_e8m0_exponent(amax);
+            s[r * nb + b] = (uint8_t)(e + 127);
+            uint8_t codes[32];
+            for (int i = 0; i < 32; i++) {
+                double v = ldexp((double)load_elem(x, dtype, base + i), -e);
+                codes[i] = or_e2m1_encode(v, ties_away);
+            }
+            for (int j = 0; j < 16; j++)
+                q[r * (k / 2) + b * 16 + j] =
+                    (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+}
+
+/* Dequantize: x_hat = E2M1(c) * 2^(s - 127), exact in double. */
+void or_mx_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows,
+                      int64_t k, double *y)
+{
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t i = 0; i < k; i++) {
+            uint8_t byte = q[r * (k / 2) + i / 2];
+            uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
+            y[r * k + i] =
+                or_e2m1_decode(c) * or_e8m0_decode(s[r * nb + i / 32]);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* NVFP4                                                               */
+/* ------------------------------------------------------------------ */
+
+/* Tensor scale [GUIDE sec. 2 and 4.1]: by the max rule s = max|x| / F_max,
+ * stored as the dequantization multiplier.  For the two-level format the
+ * largest magnitude must land on E2M1's 6 with the block scale at E4M3's
+ * 448, so F_max = 6 * 448 = 2688.  An all-zero tensor takes s_t = 1. */
+float or_nv_tensor_scale(float amax)
+{
+    if (amax == 0.0f)
+        return 1.0f;
+    return amax / 2688.0f;
+}
+
+/* Quantize rows x[rows][k] along k in blocks of 16 [GUIDE sec. 4.1]:
+ * x_hat = s_tensor * s_block * q.  fp32 order of operations:
+ *   t   = fl(6 * s_t)
+ *   s_b = E4M3(fl(amax_b / t))
+ *   d   = fl(s_t * E4M3value(s_b));  v_i = fl(x_i / d);  q_i = E2M1(v_i)
+ * and a block whose scale encodes to zero stores signed-zero codes.  With
+ * compute_gscale != 0 the tensor scale is computed and written to *gscale,
+ * otherwise *gscale is read.  Outputs q[rows][k/2], s[rows][k/16]. */
+void or_nv_quantize(const void *x, int dtype, int64_t rows, int64_t k,
+                    float *gscale, int compute_gscale, uint8_t *q, uint8_t *s)
+{
+    int64_t nb = k / 16;
+    if (compute_gscale) {
+        float amax = 0.0f;
+        for (int64_t i = 0; i < rows * k; i++) {
+            float a = fabsf(load_elem(x, dtype, i));
+            if (a > amax)
+                amax = a;
+        }
+        *gscale = or_nv_tensor_scale(amax);
+    }
+    const float st = *gscale;
+    const float t = 6.0f * st;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            int64_t base = r * k + b * 16;
+            float amax = 0.0f;
+            for (int i = 0; i < 16; i++) {
+                float a = fabsf(load_elem(x, dtype, base + i));
+                if (a > amax)
+                    amax = a;
+            }
+            float ratio = amax / t;
+            uint8_t sb = or_e4m3_encode(ratio);
+            s[r * nb + b] = sb;
+            float sbv = (float)or_e4m3_decode(sb);
+            uint8_t codes[16];
+            for (int i = 0; i < 16; i++) {
+                float xi = load_elem(x, dtype, base + i);
+                if (sbv == 0.0f) {
+                    codes[i] = (uint8_t)(signbit(xi) ? 8 : 0);
+                } else {
+                    float d = st * sbv;
+                    float v = xi / d;
+                    codes[i] = or_e2m1_encode((double)v, 0);
+                }
+            }
+            for (int j = 0; j < 8; j++)
+                q[r * (k / 2) + b * 8 + j] =
+                    (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+}
+
+/* Dequantize: x_hat = s_t * E4M3(s_b) * E2M1(c), exact in double. */
+void or_nv_dequantize(const uint8_t *q, const uint8_t *s, float gscale,
+                      int64_t rows, int64_t k, double *y)
+{
+    int64_t nb = k / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t i = 0; i < k; i++) {
+            uint8_t byte = q[r * (k / 2) + i / 2];
+            uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
+            y[r * k + i] = (double)gscale *
+                           or_e4m3_decode(s[r * nb + i / 16]) *
+                           or_e2m1_decode(c);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Products and metrics                                                */
+/* ------------------------------------------------------------------ */
+
+/* Y[i][j] = sum_k A[i][k] * B[j][k] and S[i][j] = sum_k |A[i][k] * B[j][k]|,
+ * both accumulated in double, k innermost.  A linear layer y = x W^T. */
+void or_gemm_nt(const double *A, const double *B, int64_t m, int64_t n,
+                int64_t k, double *Y, double *S)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; i++) {
+        for (int64_t j = 0; j < n; j++) {
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t t = 0; t < k; t++) {
+                double p = A[i * k + t] * B[j * k + t];
+                acc += p;
+                sabs += fabs(p);
+            }
+            Y[i * n + j] = acc;
+            if (S)
+                S[i * n + j] = sabs;
+        }
+    }
+}
+
+/* NMSE = ||x - x_hat||^2 / ||x||^2 and cosine similarity [TRANSFP4 sec. 3.2],
+ * in double over flattened tensors. */
+void or_metrics(const double *x, const double *xh, int64_t n, double *nmse,
+                double *cosine)
+{
+    double se = 0.0, xx = 0.0, hh = 0.0, xh_dot = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double d = x[i] - xh[i];
+        se += d * d;
+        xx += x[i] * x[i];
+        hh += xh[i] * xh[i];
+        xh_dot += x[i] * xh[i];
+    }
+    *nmse = se / xx;
+    *cosine = xh_dot / (sqrt(xx) * sqrt(hh));
+}
