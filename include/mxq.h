@@ -1,0 +1,179 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) MXFP4 / NVFP4 microscaling library
+ * (libmxq.so).
+ *
+ * Formats (the web pages these follow):
+ *   - MXFP4: blocks of 32 consecutive elements along a row share one E8M0
+ *     scale (a pure power of two, code c means 2^(c-127)); each element is an
+ *     E2M1 code (1 sign, 2 exponent, 1 mantissa bit; magnitudes
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}).  4.25 bits per element.
+ *     ["4.5 FP8 and NVFP4/MXFP4" (infra-guide), sec. 3.1, 3.3 and the
+ *     sec. 4.1 table; MXFP4 explainer (mingyuyang.com AI daily,
+ *     2026-08-05), sec. 3.]
+ *   - NVFP4: blocks of 16 share an E4M3 block scale, and the whole tensor
+ *     shares one FP32 scale: x_hat = s_tensor * s_block * q.  4.5 bits per
+ *     element plus the tensor scale.  [infra-guide sec. 4.1; TransFP4 page
+ *     "Portable FP4 quantization for heterogeneous accelerators",
+ *     sec. 1.1 eq. (1).]
+ *
+ * Quantization rules (the pages give the idea -- the block's largest
+ * magnitude is mapped onto the top of the E2M1 range by the shared scale,
+ * with nearest rounding -- and this library fixes the details):
+ *   MXFP4 scale exponent e = floor(log2(amax_block)) - 2, clamped to
+ *   [-127, 127] (an all-zero block gets code 0); element code =
+ *   E2M1 round-to-nearest-even of x * 2^-e, saturated to +-6, sign kept
+ *   (so -0 and tiny negatives give code 0x8).
+ *   NVFP4 tensor scale s_t = fl32(amax_tensor / 2688) (2688 = 6 * 448; 1 for
+ *   an all-zero tensor), stored as the DEQUANTIZATION multiplier; block
+ *   scale s_b = E4M3_rne_saturating(fl32(amax_block / fl32(6 * s_t)));
+ *   element code = E2M1_rne(fl32(x / fl32(s_t * s_b))), or signed zero when
+ *   s_b encodes to 0.
+ *
+ * Layout: every matrix is row-major with no padding ([rows][k], k
+ * contiguous); quantization blocks run along k.  Packed codes q[rows][k/2]
+ * hold element 2j in the LOW nibble of byte j and element 2j+1 in the high
+ * nibble.  Scales are one byte per block: s[rows][k/32] (E8M0) or
+ * s[rows][k/16] (E4M3).  Products use the linear-layer ("NT") form
+ *   Y[i][j] = sum_t X[i][t] * W[j][t].
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers on the current HIP device, except
+ *     mxq_status_string's result (a static host string).
+ *   - The caller owns every buffer.  The library never allocates, frees,
+ *     synchronizes, or keeps a pointer after the call returns.  Outputs must
+ *     not alias inputs.  Work is enqueued on `stream` (0 = default stream)
+ *     and the call returns without waiting for it.
+ *   - Validation happens before anything is launched; on any error nothing
+ *     is written.  A negative size -> MXQ_ERROR_INVALID_VALUE.  k not a
+ *     multiple of the block size -> MXQ_ERROR_INVALID_VALUE.  A NULL pointer
+ *     for a non-empty operand -> MXQ_ERROR_INVALID_VALUE.  A base pointer
+ *     that is not 16-byte aligned (4-byte for the scalar NVFP4 tensor scale)
+ *     -> MXQ_ERROR_MISALIGNED.  No HIP device, or a device that is not
+ *     gfx950 -> MXQ_ERROR_NOT_SUPPORTED.  A failed launch ->
+ *     MXQ_ERROR_LAUNCH_FAILURE.  Faults inside a kernel are asynchronous and
+ *     surface at the caller's next synchronization.
+ *   - Empty problems are no-ops that return MXQ_SUCCESS (NULL pointers are
+ *     then allowed), except that a product with k == 0 and a non-empty
+ *     output writes zeros.
+ *   - Non-finite inputs (NaN, Inf) are outside the contract.  Products whose
+ *     exact value, or whose dequantized operands, leave the fp32 range
+ *     (scale codes above 250 or below about 16) are outside the contract.
+ *   - Results are deterministic: the same call gives bitwise identical
+ *     output on every run.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_API __attribute__((visibility("default")))
+
+typedef enum {
+    MXQ_SUCCESS = 0,
+    MXQ_ERROR_INVALID_VALUE = 1,
+    MXQ_ERROR_MISALIGNED = 2,
+    MXQ_ERROR_NOT_SUPPORTED = 3,
+    MXQ_ERROR_LAUNCH_FAILURE = 4
+} mxq_status;
+
+/* Element type of an unquantized operand: fp32, or bf16 (bfloat16). */
+typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1 } mxq_dtype;
+
+/* Static, NUL-terminated description of a status code (host memory). */
+MXQ_API const char *mxq_status_string(mxq_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+MXQ_API int mxq_version(void);
+
+/*
+ * MXFP4 quantize.  x[rows][k] of type xdt (MXQ_F32 or MXQ_BF16) ->
+ * q[rows][k/2] packed E2M1 codes and s[rows][k/32] E8M0 scale codes.
+ * Online (calibration-free) quantization from 16- or 32-bit values, as in
+ * load-time conversion of a BF16 checkpoint [infra-guide sec. 4.2].
+ * k % 32 == 0 is required (32-aligned K is the kernel contract, TransFP4
+ * page sec. 2.2 Table 3).
+ */
+MXQ_API mxq_status mxq_quantize(const void *x, mxq_dtype xdt, int64_t rows, int64_t k,
+                        uint8_t *q, uint8_t *s, hipStream_t stream);
+
+/*
+ * MXFP4 dequantize.  (q[rows][k/2], s[rows][k/32]) -> y[rows][k] of type ydt:
+ * y = E2M1(code) * 2^(s - 127), exact in fp32 and bf16 for scale codes
+ * 1..250 [TransFP4 page eq. (1) with s_g = 1].  Scale code 255 (NaN in E8M0)
+ * gives NaN.
+ */
+MXQ_API mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows,
+                          int64_t k, void *y, mxq_dtype ydt,
+                          hipStream_t stream);
+
+/*
+ * W4A16 product with an MXFP4 weight: y[m][n] = sum_k x[m][k] * W_hat[n][k],
+ * where W = (wq[n][k/2], ws[n][k/32]) is dequantized in registers (never
+ * written out in 16 bits), x[m][k] is bf16, accumulation is fp32, and y is
+ * written as ydt (MXQ_F32 or MXQ_BF16, round to nearest even).  Weight-only
+ * 4-bit with 16-bit multiplies saves bandwidth, not arithmetic
+ * [infra-guide sec. 4.2 and 5].  Any m >= 1: m <= 16 takes the memory-bound
+ * decode (GEMV) kernel, larger m a bf16-MFMA GEMM tile.  k % 32 == 0.
+ */
+MXQ_API mxq_status mxq_gemv_w4a16(const uint8_t *wq, const uint8_t *ws, int64_t n,
+                          int64_t k, const void *x, int64_t m, void *y,
+                          mxq_dtype ydt, hipStream_t stream);
+
+/*
+ * W4A4 product of two MXFP4 operands on the gfx950 block-scaled MFMA:
+ * c[m][n] = sum_k A_hat[m][k] * B_hat[n][k], A = (aq[m][k/2], as[m][k/32]),
+ * B = (bq[n][k/2], bs[n][k/32]); fp32 accumulation; c written as cdt.
+ * Native FP4 matrix math needs both operands quantized [infra-guide sec. 5];
+ * CDNA 4 provides exponent-block-scaled matrix instructions [TransFP4 page
+ * sec. 5.1].  k % 32 == 0.
+ */
+MXQ_API mxq_status mxq_gemm_w4a4(const uint8_t *aq, const uint8_t *as,
+                         const uint8_t *bq, const uint8_t *bs, int64_t m,
+                         int64_t n, int64_t k, void *c, mxq_dtype cdt,
+                         hipStream_t stream);
+
+/*
+ * NVFP4 quantize.  x[rows][k] (xdt) -> q[rows][k/2] packed E2M1 codes,
+ * s[rows][k/16] E4M3 block-scale codes, and the fp32 tensor scale *gscale
+ * (a single float in device memory, the dequantization multiplier).
+ * compute_gscale != 0: the library computes s_t from the tensor's amax and
+ * writes it to *gscale (the caller's value is overwritten).  compute_gscale
+ * == 0: *gscale is read as given (a static, pre-computed scale; it must be
+ * finite and > 0).  k % 16 == 0.  [infra-guide sec. 2 and 4.1.]
+ */
+MXQ_API mxq_status nvq_quantize(const void *x, mxq_dtype xdt, int64_t rows, int64_t k,
+                        float *gscale, int compute_gscale, uint8_t *q,
+                        uint8_t *s, hipStream_t stream);
+
+/*
+ * NVFP4 dequantize: y = (*gscale) * E4M3(s) * E2M1(q), written as ydt.
+ * E4M3(s) * E2M1(q) is exact; the product with the fp32 tensor scale is
+ * rounded ONCE, to nearest even, to ydt (fp32 or bf16).  k % 16 == 0.
+ */
+MXQ_API mxq_status nvq_dequantize(const uint8_t *q, const uint8_t *s,
+                          const float *gscale, int64_t rows, int64_t k,
+                          void *y, mxq_dtype ydt, hipStream_t stream);
+
+/*
+ * W4A16 product with an NVFP4 weight, software two-level dequantization:
+ * y[m][n] = s_t * sum_k x[m][k] * (E4M3(ws[n][k/16]) * E2M1(wq[n][k])),
+ * with the block-scaled codes formed exactly in bf16 in registers, bf16
+ * MFMA with fp32 accumulation, and the tensor scale *wgscale applied once in
+ * the epilogue.  x[m][k] bf16; y written as ydt.  k % 16 == 0.
+ * [infra-guide sec. 4.1: x_hat = s_tensor * s_block * q; TransFP4 page
+ * sec. 2.5: scales are decoded at matrix load, no 16-bit copy of W.]
+ */
+MXQ_API mxq_status nvq_gemm(const uint8_t *wq, const uint8_t *ws, const float *wgscale,
+                    int64_t n, int64_t k, const void *x, int64_t m, void *y,
+                    mxq_dtype ydt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,106 @@
+// mxq_device.h -- gfx950 device-side types and codec helpers shared by the
+// library's kernels.  (The CPU oracle has its own, independent code.)
+//
+// Formats: E2M1 elements (magnitudes {0,.5,1,1.5,2,3,4,6}), E8M0 block
+// scales 2^(c-127), E4M3 block scales with max 448 and NaN only
+// ["4.5 FP8 and NVFP4/MXFP4" (infra-guide), sec. 1.2, 3.1, 4.1].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// DPP control words (quad_perm): read the value of lane (i ^ 1) / (i ^ 2)
+// inside each group of four lanes.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+__device__ __forceinline__ unsigned dpp_quad_xor1(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ unsigned dpp_quad_xor2(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false);
+}
+
+// Largest |x| of the two bf16 values packed in a dword, as bf16 magnitude
+// bits (non-negative floats order like their bit patterns).
+__device__ __forceinline__ unsigned bf16x2_absmax_bits(unsigned a, unsigned b) {
+  u16x2 ua = __builtin_bit_cast(u16x2, a & 0x7FFF7FFFu);
+  u16x2 ub = __builtin_bit_cast(u16x2, b & 0x7FFF7FFFu);
+  u16x2 m = __builtin_elementwise_max(ua, ub);
+  return __builtin_bit_cast(unsigned, m);
+}
+
+// E8M0 code for a block whose largest magnitude has exponent field `ef`
+// (the biased fp32/bf16 exponent): floor(log2 amax) - 2 clamped at -127,
+// i.e. max(ef - 2, 0).  Subnormal amax has ef == 0 and gets code 0.
+__device__ __forceinline__ unsigned e8m0_code_from_expfield(unsigned ef) {
+  return ef > 2u ? ef - 2u : 0u;
+}
+
+// The fp32 whose exponent field is the E8M0 code; the gfx950 scaled convert
+// instructions use exactly this exponent (code 0 is read as 2^-127).
+__device__ __forceinline__ float e8m0_as_scale(unsigned code) {
+  return __uint_as_float(code << 23);
+}
+
+// E4M3 (OCP FP8) value of a code: S EEEE MMM, bias 7, subnormals for
+// E = 0, and S 1111 111 is NaN.
+__device__ __forceinline__ float e4m3_value(unsigned c) {
+  unsigned e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0)
+    v = (float)m * 0x1p-9f;  // subnormal: m/8 * 2^-6
+  else if (e == 15u && m == 7u)
+    v = __builtin_nanf("");
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// E4M3 encode of r >= 0 (finite or +Inf): round to nearest, ties to even
+// mantissa, saturate at 448, underflow to 0.
+__device__ __forceinline__ unsigned e4m3_encode_nonneg(float r) {
+  if (!(r < 448.0f)) return 0x7Eu;
+  if (r < 0x1p-6f) {
+    // subnormal range: quantum 2^-9; code == number of quanta (8 == 2^-6)
+    return (unsigned)__builtin_rintf(r * 512.0f);
+  }
+  unsigned b = __float_as_uint(r);
+  unsigned rounded = b + 0x7FFFFu + ((b >> 20) & 1u);  // RNE to 3 mantissa bits
+  return (rounded >> 20) - (120u << 3);
+}
+
+// Round an fp32 to bf16 (nearest, ties to even); finite inputs.
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// bf16 rounding of the exact value p + err, where p = fl32(a*b) and
+// err = a*b - p exactly (|err| <= ulp(p)/2): a single correct rounding.
+__device__ __forceinline__ unsigned short bf16_rne_of_sum(float p, float err) {
+  unsigned u = __float_as_uint(p);
+  unsigned low = u & 0xFFFFu;
+  if (low == 0x8000u && err != 0.0f) {
+    // p sits exactly on a bf16 midpoint: the residual decides.
+    bool up = (err > 0.0f) == ((u >> 31) == 0u);  // away from zero if same sign
+    unsigned t = u >> 16;
+    return (unsigned short)(up ? t + 1u : t);
+  }
+  return f32_to_bf16_rne(p);
+}
+
+}  // namespace mxq

@@ -1,0 +1,32 @@
+// mxq_launch.h -- host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace mxq {
+
+hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
+                              hipStream_t st);
+hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y,
+                                bool bf16, hipStream_t st);
+hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,
+                              bool compute_gscale, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_nv_dequantize(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
+                                int64_t k, void* y, bool bf16, hipStream_t st);
+
+// W4A16: y[m][n] = (gscale ? *gscale : 1) * sum_k x[m][k] * deq(W)[n][k].
+// nv == false: MXFP4 weight (E8M0 per 32); nv == true: NVFP4 (E4M3 per 16).
+hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
+                        int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st);
+
+// W4A4: c[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] on the block-scaled MFMA.
+hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
+
+// Fills n elements of y (fp32 or bf16) with zeros.
+hipError_t launch_zero(void* y, int64_t n, bool bf16, hipStream_t st);
+
+}  // namespace mxq

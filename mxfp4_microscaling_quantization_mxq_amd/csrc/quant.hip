@@ -1,0 +1,293 @@
+// quant.hip -- MXFP4 and NVFP4 quantize / dequantize kernels (gfx950).
+//
+// Memory-bound elementwise work: every kernel streams its input once with
+// 16-byte loads per lane (1 KiB per wave instruction, fully coalesced) and
+// writes packed codes with 4-byte stores per lane (256 contiguous bytes per
+// wave).  The element conversion uses the CDNA4 scaled-convert
+// instructions, whose rounding (to nearest even), saturation (+-6), signed
+// zeros and subnormal handling were checked bit-exact against the CPU
+// oracle over every bf16 pattern and every E8M0 scale.
+//
+// Method [TransFP4 page "Portable FP4 quantization for heterogeneous
+// accelerators", sec. 1.1 eq. (1)]: x_hat = s_g * s_b * Q(x / (s_g * s_b)).
+#include "mxq_device.h"
+#include "mxq_launch.h"
+
+namespace mxq {
+
+// ---------------------------------------------------------------- MXFP4
+
+// One lane = 8 consecutive elements; a quad of lanes = one 32-element block
+// [infra-guide "4.5 FP8 and NVFP4/MXFP4", sec. 4.1: 32 E2M1 + one E8M0].
+// The block absmax is an integer max over magnitude bits, shared inside the
+// quad with two DPP steps; the E8M0 exponent floor(log2 amax) - 2 is read
+// straight off the exponent field.
+__global__ __launch_bounds__(256) void k_mx_quantize_bf16(const u32x4* __restrict__ x,
+                                                          unsigned* __restrict__ q,
+                                                          uint8_t* __restrict__ s,
+                                                          int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;  // nlanes is a multiple of 4: quads stay whole
+  // The convert's bf16 pairs are built from bf16x8 elements: feeding it a
+  // bit_cast<bf16x2>(uint) miscompiles (every call got the first dword).
+  bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
+  u32x4 v = __builtin_bit_cast(u32x4, xb);
+  unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
+  m = max(m & 0xFFFFu, m >> 16);
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  unsigned code = e8m0_code_from_expfield(m >> 7);
+  float scale = e8m0_as_scale(code);
+  unsigned out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[0], xb[1]}, scale, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[2], xb[3]}, scale, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[4], xb[5]}, scale, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[6], xb[7]}, scale, 3);
+  q[t] = out;
+  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+}
+
+__global__ __launch_bounds__(256) void k_mx_quantize_f32(const u32x4* __restrict__ x,
+                                                         unsigned* __restrict__ q,
+                                                         uint8_t* __restrict__ s,
+                                                         int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;
+  u32x4 a = __builtin_nontemporal_load(&x[2 * t]);
+  u32x4 b = __builtin_nontemporal_load(&x[2 * t + 1]);
+  unsigned m = max(max(max(a.x & 0x7FFFFFFFu, a.y & 0x7FFFFFFFu), max(a.z & 0x7FFFFFFFu, a.w & 0x7FFFFFFFu)),
+                   max(max(b.x & 0x7FFFFFFFu, b.y & 0x7FFFFFFFu), max(b.z & 0x7FFFFFFFu, b.w & 0x7FFFFFFFu)));
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  unsigned code = e8m0_code_from_expfield(m >> 23);
+  float scale = e8m0_as_scale(code);
+  unsigned out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(a.x), __uint_as_float(a.y), scale, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(a.z), __uint_as_float(a.w), scale, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(b.x), __uint_as_float(b.y), scale, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(b.z), __uint_as_float(b.w), scale, 3);
+  q[t] = out;
+  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+}
+
+// Dequantize: one lane = 4 code bytes = 8 elements, scale byte t/4.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restrict__ q,
+                                                       const uint8_t* __restrict__ s,
+                                                       void* __restrict__ y, int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;
+  unsigned c = q[t];
+  float scale = e8m0_as_scale(s[t >> 2]);
+  if (kBf16Out) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
+    o.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
+    o.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
+    o.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
+    ((u32x4*)y)[t] = o;
+  } else {
+    auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 0);
+    auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 1);
+    auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 2);
+    auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 3);
+    f32x4 o0 = {p0[0], p0[1], p1[0], p1[1]};
+    f32x4 o1 = {p2[0], p2[1], p3[0], p3[1]};
+    ((f32x4*)y)[2 * t] = o0;
+    ((f32x4*)y)[2 * t + 1] = o1;
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4
+
+// Tensor amax [infra-guide sec. 2: s = max|x| / F_max].  The running max is
+// kept as fp32 magnitude bits in *g (cleared by k_nv_clear first); an
+// integer atomic max is exact and order-independent.
+__global__ void k_nv_clear(unsigned* g) { *g = 0u; }
+
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_nv_amax(const u32x4* __restrict__ x, int64_t nvec,
+                                                 unsigned* __restrict__ g) {
+  unsigned m = 0;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(&x[i]);
+    if (kBf16In) {
+      unsigned h = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
+      m = max(m, max(h & 0xFFFFu, h >> 16) << 16);  // as fp32 bits
+    } else {
+      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  }
+  // wave reduction, then one atomic per wave
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(g, m);
+}
+
+// s_t from the tensor amax: fl32(amax / 2688), or 1 for an all-zero tensor.
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 2688.0f);
+}
+
+// Turns the amax bits left in *g into the tensor scale (one thread).
+__global__ void k_nv_finalize(unsigned* g) { *(float*)g = nv_tensor_scale(__uint_as_float(*g)); }
+
+// One lane = 8 consecutive elements, a pair of lanes = one 16-element block
+// [infra-guide sec. 4.1: 16 E2M1 + one E4M3, times the FP32 tensor scale].
+// fp32 order: t = fl(6 s_t); s_b = E4M3(fl(amax_b / t));
+// d = fl(s_t * s_b); q_i = E2M1_rne(fl(x_i / d)) with IEEE division.
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_nv_quantize(const u32x4* __restrict__ x,
+                                                     const unsigned* __restrict__ g,
+                                                     int amax_mode, unsigned* __restrict__ q,
+                                                     uint8_t* __restrict__ s, int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;  // nlanes is even: pairs stay whole
+  float st = amax_mode ? nv_tensor_scale(__uint_as_float(*g)) : __uint_as_float(*g);
+  float xs[8];
+  unsigned m;
+  if (kBf16In) {
+    u32x4 v = __builtin_nontemporal_load(&x[t]);
+    unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      xs[2 * i] = __uint_as_float(w[i] << 16);
+      xs[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    u32x4 a = __builtin_nontemporal_load(&x[2 * t]);
+    u32x4 b = __builtin_nontemporal_load(&x[2 * t + 1]);
+    unsigned w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) xs[i] = __uint_as_float(w[i]);
+  }
+  m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(xs[i]) & 0x7FFFFFFFu);
+  m = max(m, dpp_quad_xor1(m));
+  float tden = 6.0f * st;
+  unsigned sb = e4m3_encode_nonneg(__fdiv_rn(__uint_as_float(m), tden));
+  float sbv = e4m3_value(sb);
+  unsigned out = 0;
+  if (sbv == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) out |= (__float_as_uint(xs[i]) >> 31) << (3 + 4 * i);
+  } else {
+    float d = st * sbv;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = __fdiv_rn(xs[i], d);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], 1.0f, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], 1.0f, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], 1.0f, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], 1.0f, 3);
+  }
+  q[t] = out;
+  if ((t & 1) == 0) s[t >> 1] = (uint8_t)sb;
+}
+
+// NVFP4 dequantize: y = s_t * (s_b * q).  s_b * q is exact in fp32 (at most
+// 4 + 2 significant bits); the multiply by s_t rounds once, so fp32 output is
+// the correctly rounded exact value, and bf16 output is rounded once from
+// the exact value using the fma residual.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void k_nv_dequantize(const unsigned* __restrict__ q,
+                                                       const uint8_t* __restrict__ s,
+                                                       const float* __restrict__ g, void* __restrict__ y,
+                                                       int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;
+  float st = *g;
+  unsigned c = q[t];
+  float sbv = e4m3_value(s[t >> 1]);
+  auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+  auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+  auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+  const float r[8] = {p0[0] * sbv, p0[1] * sbv, p1[0] * sbv, p1[1] * sbv,
+                      p2[0] * sbv, p2[1] * sbv, p3[0] * sbv, p3[1] * sbv};
+  if (kBf16Out) {
+    unsigned short h[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      float p = st * r[i];
+      float e = __builtin_fmaf(st, r[i], -p);
+      h[i] = bf16_rne_of_sum(p, e);
+    }
+    u32x4 o = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
+               h[6] | ((unsigned)h[7] << 16)};
+    ((u32x4*)y)[t] = o;
+  } else {
+    f32x4 o0 = {st * r[0], st * r[1], st * r[2], st * r[3]};
+    f32x4 o1 = {st * r[4], st * r[5], st * r[6], st * r[7]};
+    ((f32x4*)y)[2 * t] = o0;
+    ((f32x4*)y)[2 * t + 1] = o1;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
+
+hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
+                              hipStream_t st) {
+  int64_t nlanes = rows * k / 8;
+  if (bf16)
+    hipLaunchKernelGGL(k_mx_quantize_bf16, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (unsigned*)q, s, nlanes);
+  else
+    hipLaunchKernelGGL(k_mx_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (unsigned*)q, s, nlanes);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y,
+                                bool bf16, hipStream_t st) {
+  int64_t nlanes = rows * k / 8;
+  if (bf16)
+    hipLaunchKernelGGL(k_mx_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const unsigned*)q, s, y, nlanes);
+  else
+    hipLaunchKernelGGL(k_mx_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const unsigned*)q, s, y, nlanes);
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,
+                              bool compute_gscale, uint8_t* q, uint8_t* s, hipStream_t st) {
+  int64_t n = rows * k;
+  int64_t nlanes = n / 8;
+  unsigned* g = (unsigned*)gscale;
+  if (compute_gscale) {
+    hipLaunchKernelGGL(k_nv_clear, dim3(1), dim3(1), 0, st, g);
+    int64_t nvec = bf16 ? n / 8 : n / 4;
+    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 256), 4096);
+    if (bf16)
+      hipLaunchKernelGGL(k_nv_amax<true>, dim3(blocks), dim3(256), 0, st, (const u32x4*)x, nvec, g);
+    else
+      hipLaunchKernelGGL(k_nv_amax<false>, dim3(blocks), dim3(256), 0, st, (const u32x4*)x, nvec, g);
+  }
+  int mode = compute_gscale ? 1 : 0;
+  if (bf16)
+    hipLaunchKernelGGL(k_nv_quantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (const unsigned*)g, mode, (unsigned*)q, s, nlanes);
+  else
+    hipLaunchKernelGGL(k_nv_quantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (const unsigned*)g, mode, (unsigned*)q, s, nlanes);
+  if (compute_gscale) hipLaunchKernelGGL(k_nv_finalize, dim3(1), dim3(1), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_dequantize(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
+                                int64_t k, void* y, bool bf16, hipStream_t st) {
+  int64_t nlanes = rows * k / 8;
+  if (bf16)
+    hipLaunchKernelGGL(k_nv_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const unsigned*)q, s, gscale, y, nlanes);
+  else
+    hipLaunchKernelGGL(k_nv_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const unsigned*)q, s, gscale, y, nlanes);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,80 @@
+"""Helpers shared by the GPU parity tests: host<->device moves and the
+product tolerance check.
+
+Tolerance (stated for products): |y - y_ref| <= 2^-20 * sum_k |x_k w_k|
+against the oracle's double-accumulated y_ref over exactly dequantized
+operands.  For fp32 output that is checked as written.  For bf16 output the
+kernel's fp32 result is rounded once to bf16, and rounding is monotone, so a
+conforming fp32 result must round into [RN_bf16(y_ref - b), RN_bf16(y_ref + b)]
+with b = 2^-20 * S; that interval is what is checked.
+"""
+import numpy as np
+
+TOL = 2.0 ** -20
+
+
+def dev(a, torch_dtype=None):
+    """numpy -> device tensor.  uint16 arrays are bf16 bit patterns."""
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    if torch_dtype is not None:
+        t = t.to(torch_dtype)
+    return t.cuda()
+
+
+def host(t):
+    """device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    import torch
+
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bf16_bits_to_f64(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(d):
+    """Round doubles to the nearest bf16 value (ties to even), returned as
+    doubles.  Valid for |d| >= 2^-126 or d == 0 and below the fp32 overflow."""
+    d = np.asarray(d, dtype=np.float64)
+    u = d.view(np.uint64)
+    r = (u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1))) & ~np.uint64((1 << 45) - 1)
+    return r.view(np.float64)
+
+
+def check_product(y_dev_np, yref, S, bf16_out, what=""):
+    """Assert the tolerance; returns the largest |err| / S seen."""
+    yref = np.asarray(yref, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    b = TOL * S
+    if bf16_out:
+        y = bf16_bits_to_f64(y_dev_np)
+        lo = f64_to_bf16_rne(yref - b)
+        hi = f64_to_bf16_rne(yref + b)
+        bad = ~((y >= lo) & (y <= hi))
+    else:
+        y = np.asarray(y_dev_np, dtype=np.float64)
+        bad = ~(np.abs(y - yref) <= b)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = [(tuple(i), float(y[tuple(i)]), float(yref[tuple(i)]), float(S[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 2^-20*S; first {detail}")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(S > 0, np.abs(y - yref) / S, 0.0)
+    return float(rel.max()) if rel.size else 0.0
+
+
+def unpack_codes(q):
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = q & 15
+    out[..., 1::2] = q >> 4
+    return out

@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every entry point include/mxq.h declares, and
+reject bad arguments with the documented status before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_microscaling_quantization_mxq_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+INVALID, MISALIGNED, NOT_SUPPORTED, SUCCESS = 1, 2, 3, 0
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation (or has an empty shape) before anything is enqueued.
+A16 = ctypes.c_void_p(0x10000)
+A16b = ctypes.c_void_p(0x20000)
+A16c = ctypes.c_void_p(0x30000)
+A16d = ctypes.c_void_p(0x40000)
+MIS = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return [s for s in re.findall(r"^MXQ_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.skip("libmxq.so not built")
+    return mxq.capi()
+
+
+def test_header_declares_the_api():
+    assert sorted(declared_symbols()) == sorted(mxq.API)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.mxq_version() == 100
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert len(mxq.status_string(code)) > 3
+    assert mxq.status_string(99) == "unknown status"
+
+
+def test_quantize_validation(lib):
+    q = lib.mxq_quantize
+    assert q(A16, 1, 4, 48, A16b, A16c, NULL) == INVALID  # k % 32
+    assert q(A16, 1, -1, 32, A16b, A16c, NULL) == INVALID
+    assert q(A16, 1, 4, -32, A16b, A16c, NULL) == INVALID
+    assert q(A16, 7, 4, 32, A16b, A16c, NULL) == INVALID  # bad dtype
+    assert q(NULL, 1, 4, 32, A16b, A16c, NULL) == INVALID
+    assert q(A16, 1, 4, 32, NULL, A16c, NULL) == INVALID
+    assert q(A16, 1, 4, 32, A16b, NULL, NULL) == INVALID
+    assert q(MIS, 1, 4, 32, A16b, A16c, NULL) == MISALIGNED
+    assert q(A16, 1, 4, 32, MIS, A16c, NULL) == MISALIGNED
+    assert q(NULL, 1, 0, 32, NULL, NULL, NULL) == SUCCESS  # empty
+    assert q(NULL, 1, 4, 0, NULL, NULL, NULL) == SUCCESS
+
+
+def test_dequantize_validation(lib):
+    d = lib.mxq_dequantize
+    assert d(A16, A16b, 4, 40, A16c, 1, NULL) == INVALID
+    assert d(A16, A16b, 4, 32, A16c, 5, NULL) == INVALID
+    assert d(A16, NULL, 4, 32, A16c, 1, NULL) == INVALID
+    assert d(A16, A16b, 4, 32, MIS, 1, NULL) == MISALIGNED
+    assert d(NULL, NULL, 0, 32, NULL, 1, NULL) == SUCCESS
+
+
+def test_gemv_and_nv_gemm_validation(lib):
+    g = lib.mxq_gemv_w4a16
+    assert g(A16, A16b, 8, 48, A16c, 1, A16d, 1, NULL) == INVALID  # MX needs k % 32
+    assert g(A16, A16b, 8, 64, A16c, -1, A16d, 1, NULL) == INVALID
+    assert g(A16, A16b, 8, 64, NULL, 1, A16d, 1, NULL) == INVALID
+    assert g(A16, A16b, 8, 64, A16c, 1, NULL, 1, NULL) == INVALID
+    assert g(A16, A16b, 8, 64, MIS, 1, A16d, 1, NULL) == MISALIGNED
+    assert g(NULL, NULL, 0, 64, NULL, 1, NULL, 1, NULL) == SUCCESS
+    assert g(NULL, NULL, 8, 64, NULL, 0, NULL, 1, NULL) == SUCCESS
+    n = lib.nvq_gemm
+    assert n(A16, A16b, NULL, 8, 48, A16c, 1, A16d, 1, NULL) == INVALID  # gscale missing
+    assert n(A16, A16b, A16c, 8, 40, A16c, 1, A16d, 1, NULL) == INVALID  # k % 16
+    assert n(A16, A16b, ctypes.c_void_p(0x50002), 8, 48, A16c, 1, A16d, 1, NULL) == MISALIGNED
+
+
+def test_w4a4_validation(lib):
+    g = lib.mxq_gemm_w4a4
+    assert g(A16, A16b, A16c, A16d, 4, 4, 33, A16, 1, NULL) == INVALID
+    assert g(A16, A16b, A16c, NULL, 4, 4, 32, A16, 1, NULL) == INVALID
+    assert g(A16, A16b, A16c, A16d, 4, 4, 32, MIS, 1, NULL) == MISALIGNED
+    assert g(A16, A16b, MIS, A16d, 4, 4, 32, A16, 1, NULL) == MISALIGNED
+    assert g(NULL, NULL, NULL, NULL, 0, 4, 32, NULL, 1, NULL) == SUCCESS
+
+
+def test_nv_quantize_validation(lib):
+    q = lib.nvq_quantize
+    assert q(A16, 1, 4, 24, A16b, 1, A16c, A16d, NULL) == INVALID
+    assert q(A16, 1, 4, 32, NULL, 1, A16c, A16d, NULL) == INVALID
+    assert q(A16, 1, 4, 32, ctypes.c_void_p(0x50001), 1, A16c, A16d, NULL) == MISALIGNED
+    assert q(NULL, 1, 0, 32, NULL, 1, NULL, NULL, NULL) == SUCCESS
+    d = lib.nvq_dequantize
+    assert d(A16, A16b, NULL, 4, 32, A16c, 1, NULL) == INVALID
+    assert d(A16, A16b, A16d, 4, 8, A16c, 1, NULL) == INVALID
+
+
+def test_no_device_reports_not_supported(lib):
+    """Valid arguments on a machine without a GPU: NOT_SUPPORTED, no launch."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case is only safe without one")
+    assert lib.mxq_quantize(A16, 1, 4, 32, A16b, A16c, NULL) == NOT_SUPPORTED
+    assert lib.mxq_gemm_w4a4(A16, A16b, A16c, A16d, 4, 4, 32, A16, 1, NULL) == NOT_SUPPORTED
+    assert lib.nvq_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, NULL) == NOT_SUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mxq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mxq, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        mxq.capi()

@@ -1,0 +1,442 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Codes and scales must be bit-exact; dequantized values exact (or rounded
+once, for NVFP4); products within 2^-20 * sum|a_i b_i| of the oracle's
+double-accumulated result (see gpu_util.check_product).  Inputs come from
+the seeded generators; the oracle quantizes its own copy of every input.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import mxfp4_microscaling_quantization_mxq_amd as mxq
+from mxfp4_microscaling_quantization_mxq_amd import synth
+
+from gpu_util import bf16_bits_to_f64, check_product, dev, f64_to_bf16_rne, host, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mxq.capi()  # raises if the library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def laplace_bf16(seed, rows, k, spread=8):
+    """Laplace rows with per-row scales 2^[-spread, spread] (bf16 bits)."""
+    rng = np.random.default_rng(seed)
+    x = rng.laplace(size=(rows, k)) * np.exp2(rng.integers(-spread, spread + 1, size=(rows, 1)))
+    return synth.f32_to_bf16_bits(x.astype(np.float32))
+
+
+def laplace_f32(seed, rows, k, spread=8):
+    rng = np.random.default_rng(seed)
+    x = rng.laplace(size=(rows, k)) * np.exp2(rng.integers(-spread, spread + 1, size=(rows, 1)))
+    return x.astype(np.float32)
+
+
+def gpu_mx_quantize(x_np):
+    q, s = mxq.quantize(dev(x_np))
+    return host(q), host(s)
+
+
+def assert_mx_codes(x_np, what):
+    q, s = gpu_mx_quantize(x_np)
+    qo, so = oracle.mx_quantize(x_np)
+    if not np.array_equal(s, so):
+        bad = np.argwhere(s != so)[:5]
+        raise AssertionError(f"{what}: scale mismatch at {bad.tolist()}: gpu {[int(s[tuple(b)]) for b in bad]} "
+                             f"oracle {[int(so[tuple(b)]) for b in bad]}")
+    if not np.array_equal(q, qo):
+        bad = np.argwhere(unpack_codes(q) != unpack_codes(qo))[:5]
+        raise AssertionError(f"{what}: code mismatch at {bad.tolist()}")
+    return qo, so
+
+
+# ------------------------------------------------------------------ MXFP4 quantize
+
+def test_mx_quantize_tiny_ref_fp32():
+    w, _ = synth.tiny_ref()
+    qo, so = assert_mx_codes(w, "tiny ref")
+    assert so.shape == (256, 16)
+    nmse, cos = oracle.metrics(w.astype(np.float64), oracle.mx_dequantize(qo, so))
+    say(f"tiny ref W: NMSE {nmse:.5f} cosine {cos:.5f}")
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (37, 160), (129, 4096), (1000, 64)])
+def test_mx_quantize_ragged_bf16_and_fp32(rows, k):
+    assert_mx_codes(laplace_bf16(rows * 7 + k, rows, k), f"bf16 {rows}x{k}")
+    assert_mx_codes(laplace_f32(rows * 11 + k, rows, k), f"f32 {rows}x{k}")
+
+
+def test_mx_quantize_edge_values():
+    x = np.zeros((8, 64), dtype=np.float32)
+    x[1, :] = -0.0
+    x[2, 0] = 2.0 ** -140  # subnormal amax -> clamped exponent
+    x[2, 1] = -(2.0 ** -149)
+    x[3, :32] = 2.0 ** -126
+    x[3, 5] = -(2.0 ** -127)
+    x[4, :] = np.float32(3.3e38)  # largest scales, saturation (finite in bf16 too)
+    x[4, 3] = -np.float32(3.0e38)
+    x[5, :] = np.float32(1.0)
+    x[5, 7] = 0.25  # ties
+    x[5, 8] = 1.25 * 0.25
+    x[6, :32] = np.array([0.0625, 0.375, 0.078125, 0.25] + [0.0] * 28, dtype=np.float32)  # worked example
+    x[7, :] = np.linspace(-7, 7, 64).astype(np.float32)
+    assert_mx_codes(x, "edge f32")
+    assert_mx_codes(synth.f32_to_bf16_bits(x), "edge bf16")
+    # the worked example row: scale 2^-4 and RNE codes [1, 6, 1, 4] x 2^-4
+    q, s = gpu_mx_quantize(x)
+    assert s[6, 0] == 123
+    assert list(unpack_codes(q)[6, :4]) == [0x2, 0x7, 0x2, 0x6]
+
+
+def test_mx_quantize_exhaustive_bf16_every_exponent():
+    """Every finite bf16 pattern x, placed in a block whose largest element is
+    F_e (the largest bf16 below 2^(e+3), so the block exponent is e), for every
+    e with |x| <= F_e."""
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    finite = np.isfinite(vals)
+    pats, vals = pats[finite].astype(np.uint16), vals[finite]
+    mag = np.abs(vals.astype(np.float64))
+    blocks = []
+    for e in range(-127, 126):
+        fe_bits = np.uint16(((e + 127 + 3) << 7) - 1)  # largest bf16 below 2^(e+3)
+        fe = float(bf16_bits_to_f64(np.array([fe_bits]))[0])
+        sel = pats[mag <= fe]
+        pad = (-len(sel)) % 31
+        sel = np.concatenate([sel, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 31)
+        blk = np.empty((sel.shape[0], 32), dtype=np.uint16)
+        blk[:, 0] = fe_bits
+        blk[:, 1:] = sel
+        blocks.append(blk)
+    allb = np.concatenate(blocks)
+    allb = np.concatenate([allb, np.zeros(((-len(allb)) % 16, 32), dtype=np.uint16)]).reshape(-1, 32 * 16)
+    say(f"exhaustive sweep: {allb.size} elements")
+    assert_mx_codes(allb, "exhaustive bf16 x exponent")
+
+
+@functools.lru_cache(maxsize=1)
+def dynamic_quantize_input():
+    return synth.dynamic_quantize()
+
+
+def test_mx_quantize_dynamic_full_size():
+    x = dynamic_quantize_input()
+    say(f"dynamic quantize input {x.shape}")
+    assert_mx_codes(x, "dynamic quantize 16384x8192")
+
+
+def test_mx_quantize_deterministic():
+    x = dev(laplace_bf16(5, 512, 1024))
+    q1, s1 = mxq.quantize(x)
+    q2, s2 = mxq.quantize(x)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------------ MXFP4 dequantize
+
+def test_mx_dequantize_every_byte_and_scale():
+    # rows = scale codes 0..254 (+255 = NaN); each row holds all 256 bytes
+    q = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    s = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 32, axis=1)
+    ref = oracle.mx_dequantize(q, s)
+    with np.errstate(over="ignore"):
+        ref32 = ref.astype(np.float32)
+        refb = f64_to_bf16_rne(ref).astype(np.float32)
+    y32 = host(mxq.dequantize(dev(q), dev(s), torch.float32))
+    yb = bf16_bits_to_f64(host(mxq.dequantize(dev(q), dev(s), torch.bfloat16))).astype(np.float32)
+    for got, exp, nm in [(y32, ref32, "fp32"), (yb, refb, "bf16")]:
+        same = (got == exp) & (np.signbit(got) == np.signbit(exp))
+        same |= np.isnan(got) & np.isnan(exp)
+        assert same.all(), f"{nm}: {np.argwhere(~same)[:5].tolist()}"
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def assert_nv(x_np, gscale, what):
+    qg, sg, gg = mxq.nv_quantize(dev(x_np), gscale)
+    qg, sg, gg = host(qg), host(sg), float(host(gg)[0])
+    qo, so, go = oracle.nv_quantize(x_np, gscale)
+    assert np.float32(gg) == np.float32(go), f"{what}: tensor scale {gg} vs {go}"
+    if not np.array_equal(sg, so):
+        bad = np.argwhere(sg != so)[:5]
+        raise AssertionError(f"{what}: E4M3 scale mismatch at {bad.tolist()}: gpu "
+                             f"{[hex(sg[tuple(b)]) for b in bad]} oracle {[hex(so[tuple(b)]) for b in bad]}")
+    if not np.array_equal(qg, qo):
+        bad = np.argwhere(unpack_codes(qg) != unpack_codes(qo))[:5]
+        raise AssertionError(f"{what}: code mismatch at {bad.tolist()}")
+    return qo, so, go
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16), (5, 48), (33, 272), (256, 4096)])
+def test_nv_quantize_ragged(rows, k):
+    xb = laplace_bf16(rows + 3 * k, rows, k)
+    xf = laplace_f32(rows + 5 * k, rows, k)
+    assert_nv(xb, None, f"nv bf16 {rows}x{k}")
+    assert_nv(xf, None, f"nv f32 {rows}x{k}")
+    assert_nv(xf, 0.0123, f"nv f32 given scale {rows}x{k}")
+
+
+def test_nv_quantize_e4m3_midpoints():
+    """Block amax placed on every E4M3 midpoint (and one ulp either side)
+    with a tensor scale that makes 6*s_t a power of two."""
+    st = None
+    for cand in range(1, 4000):
+        c = np.float32(cand / 6.0 / 64.0)
+        t = np.float32(6.0) * c
+        if t == np.float32(2.0 ** np.round(np.log2(float(t)))):
+            st = c
+            break
+    assert st is not None
+    t = float(np.float32(6.0) * st)
+    vals = sorted(oracle.e4m3_decode(c) for c in range(0x7F))
+    amaxes = []
+    for a, b in zip(vals, vals[1:]):
+        mid = np.float32((a + b) / 2 * t)
+        amaxes += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e30))]
+    amaxes += [np.float32(1000 * t), np.float32(1e-12 * t)]
+    x = np.zeros((len(amaxes), 16), dtype=np.float32)
+    rng = np.random.default_rng(9)
+    for i, a in enumerate(amaxes):
+        x[i] = (rng.uniform(-1, 1, 16) * a).astype(np.float32)
+        x[i, i % 16] = a if i % 2 else -a
+    assert_nv(x, float(st), "e4m3 midpoints")
+
+
+def test_nv_zero_tensor_and_zero_blocks():
+    x = np.zeros((4, 64), dtype=np.float32)
+    x[1, 16:32] = -0.0
+    qo, so, go = assert_nv(x, None, "zero tensor")
+    assert go == 1.0
+    x[2, 40] = 3.0
+    assert_nv(x, None, "mostly zero tensor")
+
+
+@functools.lru_cache(maxsize=1)
+def nv_vs_mx_inputs():
+    return synth.nv_vs_mx()
+
+
+def test_nv_quantize_c5_full_size():
+    w, x = nv_vs_mx_inputs()
+    assert_nv(w, None, "C5 W 8192x4096")
+    assert_nv(x, None, "C5 X 4096x4096")
+
+
+def test_nv_dequantize_rounds_once():
+    xf = laplace_f32(77, 64, 256, spread=20)
+    q, s, g = oracle.nv_quantize(xf)
+    ref = oracle.nv_dequantize(q, s, g)
+    gd = torch.tensor([g], dtype=torch.float32, device="cuda")
+    y32 = host(mxq.nv_dequantize(dev(q), dev(s), gd, torch.float32))
+    yb = bf16_bits_to_f64(host(mxq.nv_dequantize(dev(q), dev(s), gd, torch.bfloat16)))
+    assert np.array_equal(y32, ref.astype(np.float32))
+    assert np.array_equal(yb, f64_to_bf16_rne(ref))
+
+
+# ------------------------------------------------------------------ W4A16 products
+
+def mx_w4a16_case(w_np, x_bits, what, out_dtypes=(torch.float32, torch.bfloat16)):
+    """Quantize W on both sides (codes must match), run the GPU product and
+    check it against the oracle."""
+    qo, so = assert_mx_codes(w_np, what + " W")
+    wd = oracle.mx_dequantize(qo, so)
+    xd = oracle.to_f64(x_bits)
+    yref, S = oracle.gemm_nt(xd, wd)
+    worst = 0.0
+    for dt in out_dtypes:
+        y = host(mxq.gemv_w4a16(dev(qo), dev(so), dev(x_bits), dt))
+        worst = max(worst, check_product(y, yref, S, dt == torch.bfloat16, f"{what} {dt}"))
+    return yref, worst
+
+
+def test_gemv_tiny_ref():
+    w, x = synth.tiny_ref()
+    yref, worst = mx_w4a16_case(w, x, "tiny ref")
+    yexact, _ = oracle.gemm_nt(oracle.to_f64(x), w.astype(np.float64))
+    nmse, cos = oracle.metrics(yexact, yref)
+    say(f"tiny ref y: NMSE vs unquantized {nmse:.5f} cosine {cos:.5f}; worst |err|/S {worst:.3g}")
+
+
+@pytest.mark.parametrize("n,k,m", [(1, 32, 1), (17, 160, 2), (300, 4128, 4), (33, 96, 16), (65, 256, 17),
+                                   (40, 512, 33), (129, 1024, 100)])
+def test_gemv_ragged_shapes(n, k, m):
+    w = laplace_bf16(n * 13 + k, n, k)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32))
+    mx_w4a16_case(w, x, f"w4a16 n={n} k={k} m={m}")
+
+
+def test_gemv_one_hot_reproduces_weight_column():
+    w = laplace_bf16(3, 64, 256)
+    qo, so = oracle.mx_quantize(w)
+    wd = oracle.mx_dequantize(qo, so)
+    x = np.zeros((2, 256), dtype=np.uint16)
+    x[0, 17] = 0x3F80  # 1.0
+    x[1, 200] = 0xBF80  # -1.0
+    y = host(mxq.gemv_w4a16(dev(qo), dev(so), dev(x), torch.float32))
+    assert np.array_equal(y[0], wd[:, 17].astype(np.float32))
+    assert np.array_equal(y[1], -wd[:, 200].astype(np.float32))
+
+
+@functools.lru_cache(maxsize=1)
+def decode_weight():
+    w, _ = synth.decode_gemv(1)
+    qo, so = oracle.mx_quantize(w)
+    return w, qo, so
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_gemv_decode_full_size_sampled(m):
+    w, qo, so = decode_weight()
+    if m == 1:
+        q, s = gpu_mx_quantize(w)
+        assert np.array_equal(q, qo) and np.array_equal(s, so), "decode W codes"
+    _, x = synth.decode_gemv(m)
+    n, k = w.shape
+    wq, ws = dev(qo), dev(so)
+    y = host(mxq.gemv_w4a16(wq, ws, dev(x), torch.bfloat16))
+    y2 = host(mxq.gemv_w4a16(wq, ws, dev(x), torch.bfloat16))
+    assert np.array_equal(y, y2), "run-to-run determinism"
+    rng = np.random.default_rng(100 + m)
+    cols = np.sort(rng.choice(n, size=384, replace=False))
+    cols = np.unique(np.concatenate([cols, [0, n - 1]]))
+    wd = oracle.mx_dequantize(qo[cols], so[cols])
+    yref, S = oracle.gemm_nt(oracle.to_f64(x), wd)
+    worst = check_product(y[:, cols], yref, S, True, f"decode m={m}")
+    say(f"decode m={m}: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
+
+
+def test_nv_gemm_ragged():
+    for (n, k, m) in [(5, 16, 1), (40, 48, 3), (70, 272, 20), (256, 1024, 64)]:
+        w = laplace_bf16(n + k, n, k)
+        x = synth.f32_to_bf16_bits(np.random.default_rng(k).standard_normal((m, k)).astype(np.float32))
+        qo, so, go = assert_nv(w, None, f"nv gemm W {n}x{k}")
+        wd = oracle.nv_dequantize(qo, so, go)
+        yref, S = oracle.gemm_nt(oracle.to_f64(x), wd)
+        g = torch.tensor([go], dtype=torch.float32, device="cuda")
+        for dt in (torch.float32, torch.bfloat16):
+            y = host(mxq.nv_gemm(dev(qo), dev(so), g, dev(x), dt))
+            check_product(y, yref, S, dt == torch.bfloat16, f"nv gemm n={n} k={k} m={m}")
+
+
+def test_nv_vs_mx_full_size_sampled():
+    """NVFP4 and MXFP4 W4A16 GEMM on the 8192x4096 weight and 4096x4096
+    activations, outputs sampled; NMSE / cosine of each format reported."""
+    w, x = nv_vs_mx_inputs()
+    n, k = w.shape
+    m = x.shape[0]
+    rng = np.random.default_rng(55)
+    rows = np.sort(rng.choice(m, size=48, replace=False))
+    cols = np.sort(rng.choice(n, size=48, replace=False))
+    xd = oracle.to_f64(x[rows])
+    wf = oracle.to_f64(w)
+    xdev = dev(x)
+    # MXFP4
+    qo, so = oracle.mx_quantize(w)
+    y = host(mxq.gemv_w4a16(dev(qo), dev(so), xdev, torch.bfloat16))
+    wd = oracle.mx_dequantize(qo[cols], so[cols])
+    yref, S = oracle.gemm_nt(xd, wd)
+    check_product(y[np.ix_(rows, cols)], yref, S, True, "C5 MXFP4")
+    nm_mx = oracle.metrics(wf, oracle.mx_dequantize(qo, so))
+    # NVFP4
+    qn, sn, gn = oracle.nv_quantize(w)
+    g = torch.tensor([gn], dtype=torch.float32, device="cuda")
+    y = host(mxq.nv_gemm(dev(qn), dev(sn), g, xdev, torch.bfloat16))
+    wd = oracle.nv_dequantize(qn[cols], sn[cols], gn)
+    yref, S = oracle.gemm_nt(xd, wd)
+    check_product(y[np.ix_(rows, cols)], yref, S, True, "C5 NVFP4")
+    nm_nv = oracle.metrics(wf, oracle.nv_dequantize(qn, sn, gn))
+    say(f"C5 W: MXFP4 NMSE {nm_mx[0]:.5f} cos {nm_mx[1]:.5f}; NVFP4 NMSE {nm_nv[0]:.5f} cos {nm_nv[1]:.5f}")
+    assert nm_nv[0] < nm_mx[0]
+
+
+# ------------------------------------------------------------------ W4A4 GEMM
+
+def w4a4_case(a_np, b_np, what, dts=(torch.float32, torch.bfloat16)):
+    qa, sa = assert_mx_codes(a_np, what + " A")
+    qb, sb = assert_mx_codes(b_np, what + " B")
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qa, sa), oracle.mx_dequantize(qb, sb))
+    for dt in dts:
+        c = host(mxq.gemm_w4a4(dev(qa), dev(sa), dev(qb), dev(sb), dt))
+        check_product(c, yref, S, dt == torch.bfloat16, f"{what} {dt}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (31, 33, 64), (70, 90, 160), (128, 128, 256), (200, 130, 1056),
+                                   (257, 129, 96)])
+def test_w4a4_ragged(m, n, k):
+    rng = np.random.default_rng(m * n + k)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    w4a4_case(a, b, f"w4a4 {m}x{n}x{k}")
+
+
+def test_w4a4_all_16x16_code_products_exact():
+    """C[i][j] = E2M1(i) * E2M1(j) through the block-scaled MFMA (unit scales)."""
+    k = 64
+    qa = np.zeros((16, k // 2), dtype=np.uint8)
+    qa[:, 0] = np.arange(16, dtype=np.uint8)  # element 0 = code i
+    sa = np.full((16, k // 32), 127, dtype=np.uint8)
+    c = host(mxq.gemm_w4a4(dev(qa), dev(sa), dev(qa), dev(sa), torch.float32))
+    vals = np.array([oracle.e2m1_decode(i) for i in range(16)])
+    assert np.array_equal(c, np.outer(vals, vals).astype(np.float32))
+
+
+def test_w4a4_unit_scales_small_k_exact():
+    rng = np.random.default_rng(12)
+    for k in (32, 64):
+        qa = rng.integers(0, 256, size=(40, k // 2), dtype=np.uint8)
+        qb = rng.integers(0, 256, size=(50, k // 2), dtype=np.uint8)
+        sa = np.full((40, k // 32), 127, dtype=np.uint8)
+        sb = np.full((50, k // 32), 127, dtype=np.uint8)
+        yref, _ = oracle.gemm_nt(oracle.mx_dequantize(qa, sa), oracle.mx_dequantize(qb, sb))
+        c = host(mxq.gemm_w4a4(dev(qa), dev(sa), dev(qb), dev(sb), torch.float32))
+        assert np.array_equal(c.astype(np.float64), yref)
+
+
+@functools.lru_cache(maxsize=1)
+def w4a4_inputs():
+    return synth.w4a4_operands()
+
+
+def test_w4a4_full_size_sampled():
+    a, b = w4a4_inputs()
+    qa, sa = oracle.mx_quantize(a)
+    qb, sb = oracle.mx_quantize(b)
+    qga, sga = gpu_mx_quantize(a)
+    assert np.array_equal(qga, qa) and np.array_equal(sga, sa), "C4 A codes"
+    qa_d, sa_d, qb_d, sb_d = dev(qa), dev(sa), dev(qb), dev(sb)
+    c = host(mxq.gemm_w4a4(qa_d, sa_d, qb_d, sb_d, torch.bfloat16))
+    c2 = host(mxq.gemm_w4a4(qa_d, sa_d, qb_d, sb_d, torch.bfloat16))
+    assert np.array_equal(c, c2), "run-to-run determinism"
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([rng.choice(8192, 62, replace=False), [0, 8191]]))
+    cols = np.unique(np.concatenate([rng.choice(8192, 62, replace=False), [0, 8191]]))
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qa[rows], sa[rows]), oracle.mx_dequantize(qb[cols], sb[cols]))
+    worst = check_product(c[np.ix_(rows, cols)], yref, S, True, "C4 8192^3")
+    say(f"C4: {len(rows)}x{len(cols)} sampled outputs, worst |err|/S {worst:.3g}")
+
+
+def test_products_with_empty_k_write_zeros():
+    y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    e = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
+    x = torch.empty((3, 0), dtype=torch.bfloat16, device="cuda")
+    mxq.gemv_w4a16(e, e, x, y=y)
+    assert torch.count_nonzero(y).item() == 0
+    c = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    a = torch.empty((3, 0), dtype=torch.uint8, device="cuda")
+    mxq.gemm_w4a4(a, a, e, e, c=c)
+    assert torch.count_nonzero(c).item() == 0
