@@ -186,17 +186,18 @@ def gemm_w4a4(aq, as_, bq, bs, out_dtype=None, c=None):
 
 # ------------------------------------------------------------------ NVFP4
 
-def nv_quantize(x, gscale=None, q=None, s=None):
+def nv_quantize(x, gscale=None, q=None, s=None, g=None):
     """NVFP4 quantize x[rows, k] -> (q[rows, k/2], s[rows, k/16] E4M3, g[1] fp32 tensor scale).
 
-    gscale=None computes the tensor scale on the device; a float or a 1-element
-    fp32 tensor is used as given."""
+    gscale=None computes the tensor scale on the device (into g if given); a
+    float or a 1-element fp32 tensor is used as given."""
     torch = _torch()
     _need(x, "x")
     rows, k = x.shape
     compute = gscale is None
     if compute:
-        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=x.device)
     elif isinstance(gscale, (float, int)):
         g = torch.tensor([float(gscale)], dtype=torch.float32, device=x.device)
     else:

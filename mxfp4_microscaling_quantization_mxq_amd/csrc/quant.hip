@@ -119,9 +119,12 @@ __global__ __launch_bounds__(256) void k_nv_amax(const u32x4* __restrict__ x, in
       m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
     }
   }
-  // wave reduction, then one atomic per wave
+  // wave reduction, then one atomic per wave -- skipped when the running max
+  // already covers it (the max only grows, so a stale read costs at most an
+  // extra atomic); same-address atomics from every wave would serialize.
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(g, m);
+  if ((threadIdx.x & 63) == 0 && m > __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    atomicMax(g, m);
 }
 
 // s_t from the tensor amax: fl32(amax / 2688), or 1 for an all-zero tensor.
@@ -261,7 +264,7 @@ hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
   if (compute_gscale) {
     hipLaunchKernelGGL(k_nv_clear, dim3(1), dim3(1), 0, st, g);
     int64_t nvec = bf16 ? n / 8 : n / 4;
-    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 256), 4096);
+    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 256), 2048);
     if (bf16)
       hipLaunchKernelGGL(k_nv_amax<true>, dim3(blocks), dim3(256), 0, st, (const u32x4*)x, nvec, g);
     else

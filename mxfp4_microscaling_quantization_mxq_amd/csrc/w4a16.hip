@@ -12,15 +12,15 @@
 // 16x16x32 bf16 MFMA with the activations as the other operand:
 //   MFMA A (16 x 32): lane l -> activation row m = l % 16, k slots 8*(l/16)..+8
 //   MFMA B (32 x 16): lane l -> weight row n = l % 16, same k slots
-// A wave covers 16 weight rows x 128 k per step (4 MFMAs per row tile); the
-// four waves of a block split k and are summed in LDS in a fixed order, so
-// results are deterministic.
+// One "chunk" step of a wave covers 16 weight rows x 128 k (4 MFMAs per row
+// tile).  A wave keeps R row tiles x U chunks of loads in flight (all issued
+// before the first is consumed, with no branches in between), which is what
+// it takes to cover HBM latency.  The waves of a block split k round-robin
+// by chunk and are summed in LDS in a fixed order: deterministic results.
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
 namespace mxq {
-
-constexpr int kWaves = 4;
 
 // Expand one lane's 16 code bytes (32 k values) into four bf16x8 MFMA
 // operands, operand j holding k values 8j..8j+7.
@@ -54,13 +54,42 @@ __device__ __forceinline__ void dequant_chunk(u32x4 c, unsigned sbytes, bf16x8 w
   }
 }
 
-template <bool kNv, int R, bool kBf16Out>
-__global__ __launch_bounds__(256) void k_w4a16_decode(const uint8_t* __restrict__ wq,
-                                                      const uint8_t* __restrict__ ws,
-                                                      const float* __restrict__ gscale, int64_t n, int64_t k,
-                                                      const uint16_t* __restrict__ x, int64_t m,
-                                                      void* __restrict__ y) {
-  __shared__ f32x4 red[kWaves][R][64];
+// Loads of one lane for one (row tile, chunk): 16 code bytes and the scale
+// byte(s).  Invalid lanes read a valid dummy address and are zeroed by a
+// select, so the load sequence has no branches.
+template <bool kNv>
+__device__ __forceinline__ void load_chunk(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+                                           int64_t row, int64_t kb, bool valid, bool khi, int64_t kq, int64_t ks,
+                                           u32x4& codes, unsigned& sc) {
+  const int64_t r = valid ? row : 0;
+  const int64_t b = valid ? kb : 0;
+  if (!kNv) {
+    u32x4 c = __builtin_nontemporal_load((const u32x4*)(wq + r * kq + b / 2));
+    unsigned s = ws[r * ks + b / 32];
+    codes = valid ? c : (u32x4){0u, 0u, 0u, 0u};
+    sc = valid ? s : 127u;
+  } else {
+    // rows are only 8-byte aligned when k % 32 == 16; the second half of the
+    // chunk exists only if kb + 16 < k
+    const bool hi = valid && khi;
+    const u32x2* cp = (const u32x2*)(wq + r * kq + b / 2);
+    u32x2 lo = __builtin_nontemporal_load(cp);
+    u32x2 h2 = __builtin_nontemporal_load(hi ? cp + 1 : cp);
+    const uint8_t* sp = ws + r * ks + b / 16;
+    unsigned s0 = sp[0];
+    unsigned s1 = sp[hi ? 1 : 0];
+    codes = valid ? (u32x4){lo.x, lo.y, hi ? h2.x : 0u, hi ? h2.y : 0u} : (u32x4){0u, 0u, 0u, 0u};
+    sc = valid ? (s0 | (hi ? s1 << 8 : 0u)) : 0u;
+  }
+}
+
+template <bool kNv, int R, int U, int W, bool kBf16Out>
+__global__ __launch_bounds__(64 * W) void k_w4a16_decode(const uint8_t* __restrict__ wq,
+                                                         const uint8_t* __restrict__ ws,
+                                                         const float* __restrict__ gscale, int64_t n, int64_t k,
+                                                         const uint16_t* __restrict__ x, int64_t m,
+                                                         void* __restrict__ y) {
+  __shared__ f32x4 red[W][R][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * (16 * R);
@@ -69,61 +98,48 @@ __global__ __launch_bounds__(256) void k_w4a16_decode(const uint8_t* __restrict_
   const int64_t kq = k / 2;                   // code bytes per row
   const int64_t ks = kNv ? k / 16 : k / 32;  // scale bytes per row
   const bool xrow = (m0 + col) < m;
-  const uint16_t* xr = x + (m0 + col) * k;
+  const uint16_t* xr = x + (xrow ? (m0 + col) : 0) * k;
 
   f32x4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; r++) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = wave; c < nchunks; c += kWaves) {
-    const int64_t kb = c * 128 + 32 * g;  // first k of this lane's chunk
-    const bool kval = kb < k;
-    // NVFP4 allows k % 32 == 16: then the last chunk holds only 16 valid k
-    const bool khi = kb + 16 < k;
-    bf16x8 xf[4];
-    if (xrow && kval) {
-      const u32x4* xp = (const u32x4*)(xr + kb);
-      xf[0] = __builtin_bit_cast(bf16x8, xp[0]);
-      xf[1] = __builtin_bit_cast(bf16x8, xp[1]);
-      if (khi) {
-        xf[2] = __builtin_bit_cast(bf16x8, xp[2]);
-        xf[3] = __builtin_bit_cast(bf16x8, xp[3]);
-      } else {
-        xf[2] = xf[3] = (bf16x8){};
+  for (int64_t c0 = wave; c0 < nchunks; c0 += W * U) {
+    u32x4 codes[U][R];
+    unsigned sc[U][R];
+    bf16x8 xf[U][4];
+    // ---- issue every load of this step
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t kb = (c0 + (int64_t)W * u) * 128 + 32 * g;  // first k of the lane's chunk
+      const bool kval = kb < k;
+      const bool khi = kb + 16 < k;
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        const int64_t row = n0 + 16 * r + col;
+        load_chunk<kNv>(wq, ws, row, kb, kval && row < n, khi, kq, ks, codes[u][r], sc[u][r]);
       }
-    } else {
+      const bool xv = xrow && kval;
+      const u32x4* xp = (const u32x4*)(xr + (xv ? kb : 0));
+      const bool xhi = xv && khi;
 #pragma unroll
-      for (int j = 0; j < 4; j++) xf[j] = (bf16x8){};
-    }
-    u32x4 codes[R];
-    unsigned sc[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int64_t row = n0 + 16 * r + col;
-      if (row < n && kval) {
-        if (kNv) {
-          // rows are only 8-byte aligned when k % 32 == 16
-          const u32x2* cp = (const u32x2*)(wq + row * kq + kb / 2);
-          u32x2 lo = __builtin_nontemporal_load(cp);
-          u32x2 hi = khi ? __builtin_nontemporal_load(cp + 1) : (u32x2){0u, 0u};
-          codes[r] = (u32x4){lo.x, lo.y, hi.x, hi.y};
-          const uint8_t* sp = ws + row * ks + kb / 16;
-          sc[r] = sp[0] | (khi ? ((unsigned)sp[1] << 8) : 0u);
-        } else {
-          codes[r] = __builtin_nontemporal_load((const u32x4*)(wq + row * kq + kb / 2));
-          sc[r] = ws[row * ks + kb / 32];
-        }
-      } else {
-        codes[r] = (u32x4){0u, 0u, 0u, 0u};
-        sc[r] = kNv ? 0u : 127u;
+      for (int j = 0; j < 4; j++) {
+        u32x4 v = xp[(j < 2 || xhi) ? j : 0];
+        const bool ok = j < 2 ? xv : xhi;
+        xf[u][j] = __builtin_bit_cast(bf16x8, ok ? v : (u32x4){0u, 0u, 0u, 0u});
       }
     }
+    // ---- consume
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      bf16x8 wf[4];
-      dequant_chunk<kNv>(codes[r], sc[r], wf);
+    for (int u = 0; u < U; u++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[j], wf[j], acc[r], 0, 0, 0);
+      for (int r = 0; r < R; r++) {
+        bf16x8 wf[4];
+        dequant_chunk<kNv>(codes[u][r], sc[u][r], wf);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][j], wf[j], acc[r], 0, 0, 0);
+      }
     }
   }
 
@@ -131,11 +147,11 @@ __global__ __launch_bounds__(256) void k_w4a16_decode(const uint8_t* __restrict_
   for (int r = 0; r < R; r++) red[wave][r][lane] = acc[r];
   __syncthreads();
   const float st = kNv ? *gscale : 1.0f;
-  for (int idx = threadIdx.x; idx < R * 64; idx += 256) {
+  for (int idx = threadIdx.x; idx < R * 64; idx += 64 * W) {
     const int r = idx >> 6, l = idx & 63;
     f32x4 v = red[0][r][l];
 #pragma unroll
-    for (int w = 1; w < kWaves; w++) v += red[w][r][l];
+    for (int w = 1; w < W; w++) v += red[w][r][l];
     const int64_t nn = n0 + 16 * r + (l & 15);
     if (nn >= n) continue;
 #pragma unroll
@@ -151,24 +167,163 @@ __global__ __launch_bounds__(256) void k_w4a16_decode(const uint8_t* __restrict_
   }
 }
 
-template <bool kNv, int R>
+// ---------------------------------------------------------------------------
+// Decode kernel for m <= 4 (vector ALU).  HBM efficiency decides this path:
+// each wave load instruction reads 1 KiB of ONE weight row (lane l: the 16
+// code bytes of k = kr*2048 + 32l .. +32, plus that block's scale byte), the
+// same access pattern as a linear stream.  Lane l keeps the activations of
+// its 32 k values in registers for the whole row sweep; per row it expands
+// its codes to exact (unscaled) E2M1 values in bf16 and accumulates
+// v_dot2_f32_bf16 products, then applies the block scale with one fp32 FMA
+// (MXFP4: 2^e, exact; NVFP4: the E4M3 block scale, per 16).  Each lane ends
+// with one partial sum per (activation row, weight row); the 64 lanes x W
+// waves are summed through LDS in a fixed order.
+template <bool kNv, int M, int RB, int U, int W, bool kBf16Out>
+__global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __restrict__ wq,
+                                                              const uint8_t* __restrict__ ws,
+                                                              const float* __restrict__ gscale, int64_t n,
+                                                              int64_t k, const uint16_t* __restrict__ x,
+                                                              void* __restrict__ y) {
+  static_assert(RB % U == 0, "rows per block must be a multiple of the unroll");
+  // per-wave partial sums: red[wave][act row][weight row][lane]
+  __shared__ float red[W][M][RB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * RB;
+  const int64_t kq = k / 2;                   // code bytes per row
+  const int64_t ks = kNv ? k / 16 : k / 32;  // scale bytes per row
+  const int64_t nkr = (k + 2047) / 2048;      // k ranges of 64 lanes x 32
+
+  for (int mm = 0; mm < M; mm++)
+    for (int r = 0; r < RB; r++) red[wave][mm][r][lane] = 0.f;
+
+  for (int64_t kr = wave; kr < nkr; kr += W) {
+    const int64_t kb = kr * 2048 + 32 * lane;  // this lane's 32 k values
+    const bool kval = kb < k;
+    const bool khi = kb + 16 < k;  // NVFP4 may end on a half chunk
+    // activations of this lane's k values: 16 bf16 pairs per activation row
+    bf16x2 xs[M][16];
+#pragma unroll
+    for (int mm = 0; mm < M; mm++) {
+      const bf16x8* xp = (const bf16x8*)(x + mm * k + (kval ? kb : 0));
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bool ok = kval && (j < 2 || khi);
+        bf16x8 v = xp[ok ? j : 0];
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+          xs[mm][4 * j + p] = ok ? (bf16x2){v[2 * p], v[2 * p + 1]} : (bf16x2){(__bf16)0.f, (__bf16)0.f};
+      }
+    }
+#pragma unroll 1
+    for (int r0 = 0; r0 < RB; r0 += U) {
+      u32x4 codes[U];
+      unsigned sc[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int64_t row = n0 + r0 + u;
+        load_chunk<kNv>(wq, ws, row, kb, kval && row < n, khi, kq, ks, codes[u], sc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const unsigned d[4] = {codes[u].x, codes[u].y, codes[u].z, codes[u].w};
+        bf16x2 w[16];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 0);
+          w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 1);
+          w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 2);
+          w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 3);
+        }
+#pragma unroll
+        for (int mm = 0; mm < M; mm++) {
+          float acc = red[wave][mm][r0 + u][lane];
+          if (!kNv) {
+            float p = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i++) p = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p, false);
+            acc = __builtin_fmaf(p, e8m0_as_scale(sc[u] & 0xFFu), acc);
+          } else {
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) p0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p0, false);
+#pragma unroll
+            for (int i = 8; i < 16; i++) p1 = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p1, false);
+            acc = __builtin_fmaf(p0, e4m3_value(sc[u] & 0xFFu), acc);
+            acc = __builtin_fmaf(p1, e4m3_value((sc[u] >> 8) & 0xFFu), acc);
+          }
+          red[wave][mm][r0 + u][lane] = acc;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // sum of W x 64 partials per output, 8 threads per output, fixed order
+  const float st = kNv ? *gscale : 1.0f;
+  for (int o = threadIdx.x >> 3; o < M * RB; o += 8 * W) {
+    const int part = threadIdx.x & 7;
+    const int mm = o / RB, r = o % RB;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; w++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) v += red[w][mm][r][part * 8 + i];
+    v += __shfl_xor(v, 1, 8);
+    v += __shfl_xor(v, 2, 8);
+    v += __shfl_xor(v, 4, 8);
+    const int64_t nn = n0 + r;
+    if (part == 0 && nn < n) {
+      const float out = kNv ? v * st : v;
+      if (kBf16Out)
+        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(out);
+      else
+        ((float*)y)[mm * n + nn] = out;
+    }
+  }
+}
+
+template <bool kNv, int M>
+static void launch_decode_valu(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
+                               const void* x, void* y, bool bf16_out, hipStream_t st) {
+  constexpr int RB = M <= 2 ? 16 : 8, U = 8, W = 4;
+  dim3 grid((unsigned)((n + RB - 1) / RB));
+  if (bf16_out)
+    hipLaunchKernelGGL((k_w4a16_decode_valu<kNv, M, RB, U, W, true>), grid, dim3(64 * W), 0, st, wq, ws, gscale,
+                       n, k, (const uint16_t*)x, y);
+  else
+    hipLaunchKernelGGL((k_w4a16_decode_valu<kNv, M, RB, U, W, false>), grid, dim3(64 * W), 0, st, wq, ws, gscale,
+                       n, k, (const uint16_t*)x, y);
+}
+
+template <bool kNv, int R, int U, int W>
 static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                           const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   dim3 grid((unsigned)((n + 16 * R - 1) / (16 * R)), (unsigned)((m + 15) / 16));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_decode<kNv, R, true>), grid, dim3(256), 0, st, wq, ws, gscale, n, k,
+    hipLaunchKernelGGL((k_w4a16_decode<kNv, R, U, W, true>), grid, dim3(64 * W), 0, st, wq, ws, gscale, n, k,
                        (const uint16_t*)x, m, y);
   else
-    hipLaunchKernelGGL((k_w4a16_decode<kNv, R, false>), grid, dim3(256), 0, st, wq, ws, gscale, n, k,
+    hipLaunchKernelGGL((k_w4a16_decode<kNv, R, U, W, false>), grid, dim3(64 * W), 0, st, wq, ws, gscale, n, k,
                        (const uint16_t*)x, m, y);
 }
 
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  if (nv)
-    launch_decode<true, 2>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
-  else
-    launch_decode<false, 2>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  if (m <= 4) {
+    switch ((int)m) {
+      case 1: nv ? launch_decode_valu<true, 1>(wq, ws, gscale, n, k, x, y, bf16_out, st)
+                 : launch_decode_valu<false, 1>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
+      case 2: nv ? launch_decode_valu<true, 2>(wq, ws, gscale, n, k, x, y, bf16_out, st)
+                 : launch_decode_valu<false, 2>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
+      case 3: nv ? launch_decode_valu<true, 3>(wq, ws, gscale, n, k, x, y, bf16_out, st)
+                 : launch_decode_valu<false, 3>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
+      default: nv ? launch_decode_valu<true, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st)
+                  : launch_decode_valu<false, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
+    }
+  } else if (nv) {
+    launch_decode<true, 2, 2, 4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  } else {
+    launch_decode<false, 2, 4, 4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  }
   return hipGetLastError();
 }
 
