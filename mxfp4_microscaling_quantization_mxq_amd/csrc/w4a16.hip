@@ -284,7 +284,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
 template <bool kNv, int M>
 static void launch_decode_valu(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                                const void* x, void* y, bool bf16_out, hipStream_t st) {
-  constexpr int RB = M <= 2 ? 16 : 8, U = 8, W = 4;
+  constexpr int RB = M == 1 ? 8 : 16, U = 8, W = 4;
   dim3 grid((unsigned)((n + RB - 1) / RB));
   if (bf16_out)
     hipLaunchKernelGGL((k_w4a16_decode_valu<kNv, M, RB, U, W, true>), grid, dim3(64 * W), 0, st, wq, ws, gscale,
