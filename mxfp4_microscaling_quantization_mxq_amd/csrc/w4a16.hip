@@ -294,6 +294,210 @@ static void launch_decode_valu(const uint8_t* wq, const uint8_t* ws, const float
                        n, k, (const uint16_t*)x, y);
 }
 
+// ---------------------------------------------------------------------------
+// GEMM kernel (large m, k % 64 == 0): bf16 MFMA, MFMA-bound.
+// Block tile 256 (x rows) x 256 (weight rows), four waves of 128 x 128, each
+// a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 per 16-k step.  k advances in
+// stages of 64 through a ring of three LDS stages filled by direct
+// global -> LDS loads (global_load_lds_dwordx4):
+//   * x: 256 rows x 128 B per stage, 16-B unit u of row r stored at
+//     u ^ ((r >> 1) & 7) (conflict-free fragment reads);
+//   * weight codes: 256 rows x 32 B per stage, unit u at u ^ ((r >> 3) & 1).
+// MFMA k slots are permuted so that a lane's 8 k values of step kk are
+// k = 32*half + 8*kk + 0..7: its weight codes for the whole stage are then
+// one 16-B chunk = one MXFP4 block (two NVFP4 blocks), dequantized per step
+// in registers -- MXFP4 with the scaled convert (exact bf16), NVFP4 as
+// E4M3 * E2M1 in fp32 (exact, <= 6 significant bits) -- and x is read with
+// the same permutation.  Operands are swapped (weight rows on the
+// instruction's A side) so a lane stores four consecutive outputs at once.
+// The NVFP4 tensor scale multiplies the fp32 result in the epilogue.
+constexpr int kGBM = 256, kGBN = 256, kGRing = 3;
+constexpr int kGXStage = kGBM * 128, kGWStage = kGBN * 32;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void gdma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void gwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool kNv, bool kBf16Out>
+__global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+                                                       const float* __restrict__ gscale, int64_t n, int64_t k,
+                                                       const uint16_t* __restrict__ x, int64_t m,
+                                                       void* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t xring[kGRing][kGXStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t wring[kGRing][kGWStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, r32 = lane & 31;
+
+  const int64_t tm_n = (m + kGBM - 1) / kGBM, tn_n = (n + kGBN - 1) / kGBN;
+  const int64_t tiles = tm_n * tn_n;
+  int64_t tl = blockIdx.x;
+  if (tiles % 8 == 0) tl = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  const int64_t per_group = 4 * tn_n;
+  const int64_t g0 = (tl / per_group) * 4;
+  const int64_t gsz = (tm_n - g0) < 4 ? (tm_n - g0) : 4;
+  const int64_t m0 = (g0 + (tl % per_group) % gsz) * kGBM;
+  const int64_t n0 = ((tl % per_group) / gsz) * kGBN;
+  const int rows_x = (int)min((int64_t)kGBM, m - m0), rows_w = (int)min((int64_t)kGBN, n - n0);
+
+  const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
+  const int nstages = (int)(k / 64);
+
+  // 10 DMA instructions per wave per stage: 8 for x, 2 for weight codes
+  // stage s into ring slot b (near the end the stage index is clamped to the
+  // last stage so every step issues the same number of loads; the copy lands
+  // in the free slot and is never read)
+  auto issue = [&](int s, int b) {
+    uint8_t* xb = xring[b];
+    uint8_t* wb = wring[b];
+    const uint8_t* sx = (const uint8_t*)x + m0 * kx + (int64_t)s * 128;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int row = 64 * wave + 8 * j + (lane >> 3);
+      const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
+      gdma16(sx + (unsigned)min(row, rows_x - 1) * (unsigned)kx + cu16, xb + (64 * wave + 8 * j) * 128);
+    }
+    const uint8_t* sw = wq + n0 * kq + (int64_t)s * 32;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int row = 64 * wave + 32 * j + (lane >> 1);
+      const unsigned cu16 = (unsigned)(((lane & 1) ^ ((row >> 3) & 1)) << 4);
+      gdma16(sw + (unsigned)min(row, rows_w - 1) * (unsigned)kq + cu16, wb + (64 * wave + 32 * j) * 32);
+    }
+  };
+  // this lane's scale byte(s) for its four weight rows at stage s (global,
+  // L2-resident): MXFP4 block 2s + half; NVFP4 blocks 4s + 2 half + {0, 1}
+  auto load_scales = [&](int s, unsigned sc[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t row = min(n0 + wn * 128 + j * 32 + r32, n - 1);
+      if (kNv) {
+        const uint8_t* p = ws + row * ks + 4 * (int64_t)s + 2 * half;
+        sc[j] = p[0] | ((unsigned)p[1] << 8);
+      } else {
+        sc[j] = ws[row * ks + 2 * (int64_t)s + half];
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+
+  const int swz = (r32 >> 1) & 7;
+  const int laneX = (wm * 128 + r32) * 128;
+  const int laneW = (wn * 128 + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
+
+  auto compute = [&](int s, const unsigned sc[4]) {
+    const uint8_t* xb = xring[s % kGRing];
+    const uint8_t* wb = wring[s % kGRing];
+    u32x4 wc[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      bf16x8 xf[4], wf[4];
+      const int unit16 = ((4 * half + kk) ^ swz) << 4;
+#pragma unroll
+      for (int i = 0; i < 4; i++) xf[i] = *(const bf16x8*)(xb + laneX + i * 32 * 128 + unit16);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const unsigned d = kk == 0 ? wc[j].x : kk == 1 ? wc[j].y : kk == 2 ? wc[j].z : wc[j].w;
+        if (!kNv) {
+          const float scale = e8m0_as_scale(sc[j] & 0xFFu);
+          bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+          bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+          bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+          bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+          wf[j] = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+          const float sb = e4m3_value(kk < 2 ? (sc[j] & 0xFFu) : ((sc[j] >> 8) & 0xFFu));
+          auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+          auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+          auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+          auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+          wf[j] = (bf16x8){(__bf16)(p0[0] * sb), (__bf16)(p0[1] * sb), (__bf16)(p1[0] * sb), (__bf16)(p1[1] * sb),
+                           (__bf16)(p2[0] * sb), (__bf16)(p2[1] * sb), (__bf16)(p3[0] * sb), (__bf16)(p3[1] * sb)};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // prologue: stages 0, 1 in flight
+  issue(0, 0);
+  issue(min(1, nstages - 1), 1);
+  unsigned sc_cur[4], sc_nxt[4];
+  load_scales(0, sc_cur);
+  for (int s = 0; s < nstages; s++) {
+    load_scales(min(s + 1, nstages - 1), sc_nxt);
+    gwait_vmcnt<10 + 4>();  // stage s landed; stage s+1 and the 4 scale loads may be in flight
+    __builtin_amdgcn_s_barrier();  // no fence: the prefetched stages stay in flight
+    issue(min(s + kGRing - 1, nstages - 1), (s + kGRing - 1) % kGRing);
+    compute(s, sc_cur);
+#pragma unroll
+    for (int j = 0; j < 4; j++) sc_cur[j] = sc_nxt[j];
+  }
+  gwait_vmcnt<0>();
+
+  const float st = kNv ? *gscale : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int64_t row = m0 + wm * 128 + i * 32 + r32;
+    if (row >= m) continue;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int64_t col = n0 + wn * 128 + j * 32 + q * 8 + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] = kNv ? acc[i][j][4 * q + e] * st : acc[i][j][4 * q + e];
+        if (col + 3 < n) {
+          if (kBf16Out) {
+            u32x2 o = {f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16),
+                       f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16)};
+            *(u32x2*)((uint16_t*)y + row * n + col) = o;
+          } else {
+            *(f32x4*)((float*)y + row * n + col) = (f32x4){v[0], v[1], v[2], v[3]};
+          }
+        } else {
+          for (int e = 0; e < 4 && col + e < n; e++) {
+            if (kBf16Out)
+              ((uint16_t*)y)[row * n + col + e] = f32_to_bf16_rne(v[e]);
+            else
+              ((float*)y)[row * n + col + e] = v[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool kNv>
+static void launch_gemm(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
+                        const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
+  const unsigned tiles = (unsigned)(((m + kGBM - 1) / kGBM) * ((n + kGBN - 1) / kGBN));
+  if (bf16_out)
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, true>), dim3(tiles), dim3(256), 0, st, wq, ws, gscale, n, k,
+                       (const uint16_t*)x, m, y);
+  else
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, false>), dim3(tiles), dim3(256), 0, st, wq, ws, gscale, n, k,
+                       (const uint16_t*)x, m, y);
+}
+
 template <bool kNv, int R, int U, int W>
 static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                           const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
@@ -319,6 +523,9 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
       default: nv ? launch_decode_valu<true, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st)
                   : launch_decode_valu<false, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
     }
+  } else if (m >= 128 && k % 64 == 0) {
+    nv ? launch_gemm<true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
+       : launch_gemm<false>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (nv) {
     launch_decode<true, 2, 2, 4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else {
