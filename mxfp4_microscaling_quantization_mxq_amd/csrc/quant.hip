@@ -106,8 +106,9 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restric
 __global__ void k_nv_clear(unsigned* g) { *g = 0u; }
 
 template <bool kBf16In>
-__global__ __launch_bounds__(256) void k_nv_amax(const u32x4* __restrict__ x, int64_t nvec,
+__global__ __launch_bounds__(512) void k_nv_amax(const u32x4* __restrict__ x, int64_t nvec,
                                                  unsigned* __restrict__ g) {
+  __shared__ unsigned wmax[8];
   unsigned m = 0;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
@@ -119,12 +120,16 @@ __global__ __launch_bounds__(256) void k_nv_amax(const u32x4* __restrict__ x, in
       m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
     }
   }
-  // wave reduction, then one atomic per wave -- skipped when the running max
-  // already covers it (the max only grows, so a stale read costs at most an
-  // extra atomic); same-address atomics from every wave would serialize.
+  // wave, then block reduction; one atomic per block (same-address atomics
+  // serialize in L2, so their number is kept to the grid size)
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0 && m > __hip_atomic_load(g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-    atomicMax(g, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned b = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); w++) b = max(b, wmax[w]);
+    if (b) atomicMax(g, b);
+  }
 }
 
 // s_t from the tensor amax: fl32(amax / 2688), or 1 for an all-zero tensor.
@@ -264,11 +269,11 @@ hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
   if (compute_gscale) {
     hipLaunchKernelGGL(k_nv_clear, dim3(1), dim3(1), 0, st, g);
     int64_t nvec = bf16 ? n / 8 : n / 4;
-    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 256), 2048);
+    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 512), 256);
     if (bf16)
-      hipLaunchKernelGGL(k_nv_amax<true>, dim3(blocks), dim3(256), 0, st, (const u32x4*)x, nvec, g);
+      hipLaunchKernelGGL(k_nv_amax<true>, dim3(blocks), dim3(512), 0, st, (const u32x4*)x, nvec, g);
     else
-      hipLaunchKernelGGL(k_nv_amax<false>, dim3(blocks), dim3(256), 0, st, (const u32x4*)x, nvec, g);
+      hipLaunchKernelGGL(k_nv_amax<false>, dim3(blocks), dim3(512), 0, st, (const u32x4*)x, nvec, g);
   }
   int mode = compute_gscale ? 1 : 0;
   if (bf16)

@@ -295,6 +295,119 @@ static void launch_decode_valu(const uint8_t* wq, const uint8_t* ws, const float
 }
 
 // ---------------------------------------------------------------------------
+// Decode kernel for 2 <= m <= 16 (MXFP4, bf16 MFMA).  Same row-contiguous
+// weight stream as the vector-ALU kernel -- each wave load instruction reads
+// 1 KiB of one row (lane l: 16 code bytes of k = kr*2048 + 32 l .. +32) and
+// the row's 64 scale bytes for that range -- but the arithmetic is the
+// 16x16x32 bf16 MFMA, whose cost does not grow with m.
+//   * a wave owns 16 weight rows for the whole k; the block (4 waves, 64
+//     rows) walks k in ranges of 2048;
+//   * per range the block stages the activation slice x[0..m)[range] in LDS
+//     once (shared by the four waves), and each wave writes its 16 x 1 KiB
+//     code tile to its own LDS region (rows padded by 16 B) and reads it back
+//     in the MFMA operand layout: lane (col, g) takes row col, 32-k block
+//     4c + g of chunk c, dequantized in registers as in the tiled kernel;
+//   * the next range's codes, scales and activations are loaded into
+//     registers while the current range is multiplied.
+// Each wave's 16 x 16 accumulator covers all of k: no cross-wave sum.
+constexpr int kDRow = 1024 + 16;  // LDS pitch of one 1 KiB code row
+constexpr int kXRow = 4096 + 16;  // LDS pitch of one activation row slice (2048 bf16)
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void k_w4a16_decode_mfma(const uint8_t* __restrict__ wq,
+                                                           const uint8_t* __restrict__ ws, int64_t n, int64_t k,
+                                                           const uint16_t* __restrict__ x, int64_t m,
+                                                           void* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes_lds[4][16 * kDRow];
+  __shared__ uint8_t scale_lds[4][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t x_lds[16 * kXRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t nw0 = (int64_t)blockIdx.x * 64 + 16 * wave;  // this wave's first row
+  const int64_t kq = k / 2, ks = k / 32;
+  const int nkr = (int)((k + 2047) / 2048);
+  uint8_t* cl = codes_lds[wave];
+  const int xm = (int)min((int64_t)col, m - 1);  // activation row of this lane
+
+  // register staging of one range: 16 code chunks + 16 scale bytes per
+  // lane, and up to 16 activation pieces of 16 B per thread
+  u32x4 c[16];
+  unsigned sc[16];
+  u32x4 xv[16];
+  auto load_range = [&](int kr) {
+    const int64_t kb = (int64_t)kr * 2048 + 32 * lane;
+    const bool kval = kb < k;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int64_t row = nw0 + r;
+      const bool v = kval && row < n;
+      const int64_t rr = v ? row : 0, bb = v ? kb : 0;
+      u32x4 t = __builtin_nontemporal_load((const u32x4*)(wq + rr * kq + bb / 2));
+      unsigned sv = ws[rr * ks + bb / 32];
+      c[r] = v ? t : (u32x4){0u, 0u, 0u, 0u};
+      sc[r] = v ? sv : 127u;
+    }
+    // activation slice: m rows x 4 KiB, 16 B per thread per row
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int64_t kk = (int64_t)kr * 2048 + 8 * tid;
+      const bool v = r < m && kk < k;
+      const u32x4 t = *(const u32x4*)(x + (v ? r * k + kk : 0));
+      xv[r] = v ? t : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_range = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      *(u32x4*)(cl + r * kDRow + 16 * lane) = c[r];
+      scale_lds[wave][r][lane] = (uint8_t)sc[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      if (r < m) *(u32x4*)(x_lds + r * kXRow + 16 * tid) = xv[r];
+  };
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  load_range(0);
+  for (int kr = 0; kr < nkr; kr++) {
+    store_range();
+    __syncthreads();  // activation slice and code tiles in LDS
+    if (kr + 1 < nkr) load_range(kr + 1);
+    const int nch = (int)min((int64_t)16, (k - (int64_t)kr * 2048 + 127) / 128);
+    for (int ch = 0; ch < nch; ch++) {
+      const int blk = 4 * ch + g;  // this lane's 32-k block within the range
+      const u32x4 cw = *(const u32x4*)(cl + col * kDRow + blk * 16);
+      const float scale = e8m0_as_scale(scale_lds[wave][col][blk]);
+      const bf16x8* xp = (const bf16x8*)(x_lds + xm * kXRow + blk * 64);
+      const unsigned d[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
+        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
+        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
+        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
+        const bf16x8 wf = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[j], wf, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done reading before the next range lands
+  }
+  // lane holds y[4g + i][nw0 + col]
+  const int64_t nn = nw0 + col;
+  if (nn < n) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t mm = 4 * g + i;
+      if (mm >= m) continue;
+      if (kBf16Out)
+        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(acc[i]);
+      else
+        ((float*)y)[mm * n + nn] = acc[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // GEMM kernel (large m, k % 64 == 0): bf16 MFMA, MFMA-bound.
 // Block tile 256 (x rows) x 256 (weight rows), four waves of 128 x 128, each
 // a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 per 16-k step.  k advances in
@@ -512,7 +625,13 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  if (m <= 4) {
+  if (!nv && m >= 5 && m <= 16) {
+    const dim3 grid((unsigned)((n + 63) / 64));
+    if (bf16_out)
+      hipLaunchKernelGGL(k_w4a16_decode_mfma<true>, grid, dim3(256), 0, st, wq, ws, n, k, (const uint16_t*)x, m, y);
+    else
+      hipLaunchKernelGGL(k_w4a16_decode_mfma<false>, grid, dim3(256), 0, st, wq, ws, n, k, (const uint16_t*)x, m, y);
+  } else if (m <= 4) {
     switch ((int)m) {
       case 1: nv ? launch_decode_valu<true, 1>(wq, ws, gscale, n, k, x, y, bf16_out, st)
                  : launch_decode_valu<false, 1>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;

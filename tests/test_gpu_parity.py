@@ -273,6 +273,7 @@ def test_gemv_tiny_ref():
 
 
 @pytest.mark.parametrize("n,k,m", [(1, 32, 1), (17, 160, 2), (300, 4128, 4), (33, 96, 16), (65, 256, 17),
+                                   (100, 2080, 5), (70, 4096, 8), (130, 8192, 16), (64, 6144, 11),
                                    (40, 512, 33), (129, 1024, 100), (300, 320, 130), (513, 64, 257),
                                    (256, 1024, 512), (1, 64, 128)])
 def test_gemv_ragged_shapes(n, k, m):
