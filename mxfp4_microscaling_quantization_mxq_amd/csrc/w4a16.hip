@@ -17,6 +17,8 @@
 // before the first is consumed, with no branches in between), which is what
 // it takes to cover HBM latency.  The waves of a block split k round-robin
 // by chunk and are summed in LDS in a fixed order: deterministic results.
+#include <type_traits>
+
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -623,9 +625,219 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
                        (const uint16_t*)x, m, y);
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel for m <= 16, k % 512 == 0 (MXFP4): the weight stream is
+// moved by direct global -> LDS loads, so the bytes in flight are bounded by
+// LDS, not by staging registers, and the arithmetic is the 16x16x32 bf16
+// MFMA (its cost does not grow with m; rows m..15 of the activation operand
+// read a shared zero row).
+//   * A block is NW waves; wave w owns weight rows n0 + 16w .. +16 for the
+//     whole of k.  k advances in stages of 512 (256 code bytes and 16 scale
+//     bytes per row, 1 KiB of activations per activation row) through a ring
+//     of NR LDS stages.
+//   * Every wave loads its own rows' codes (4 x 1 KiB, four 256-B row
+//     segments per instruction) and scales (one 4-byte-per-lane instruction
+//     = 16 rows x 16 B), and its share of the activation rows (one 1 KiB
+//     instruction per row; every wave issues the same number, surplus ones
+//     fill a scratch row, so the wait counts are compile-time constants).
+//   * LDS swizzles (applied on the global side of the copy): code unit u of
+//     row r sits at slot u ^ (r & 15); activation unit u of row i at
+//     u ^ (i & 15).  The 16 lanes of a fragment read touch 16 distinct bank
+//     groups.
+//   * Fragments: lane (col = l % 16, g = l / 16) takes code unit 4i + g of
+//     its weight row (32 k = one MXFP4 block, i = 0..3), expands it with the
+//     scaled convert to four exact bf16x8 operands, and pairs operand j with
+//     activation unit 16i + 4g + j of activation row col (the MFMA k slots
+//     are a permutation of the stage's k, the same on both sides).
+//   * One s_barrier per stage (after the wave's own copies of stage s have
+//     landed) makes the other waves' activation copies visible and frees the
+//     ring slot for the copy of stage s + NR - 1.
+constexpr int kDdK = 512;             // k per stage
+constexpr int kDdRowB = kDdK / 2;     // code bytes per row per stage
+constexpr int kDdScB = kDdK / 32;     // scale bytes per row per stage
+constexpr int kDdXRowB = kDdK * 2;    // activation bytes per row per stage
+
+__device__ __forceinline__ void gdma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// One ring slot: codes, activations and scales of one stage.  Every slot is
+// its own LDS variable and every slot index below is a compile-time
+// constant, so the compiler can tell that the reads of slot b do not touch
+// the slots whose copies are still in flight (one shared array would make it
+// wait for every outstanding copy before the first read).
+template <int MT, int NW>
+struct DdSlot {
+  uint8_t w[16 * NW * kDdRowB];
+  uint8_t x[(MT + 2) * kDdXRowB];  // MT activation rows, a zero row, a scratch row
+  uint8_t s[16 * NW * kDdScB];
+};
+template <int MT, int NW, int B>
+__device__ __forceinline__ DdSlot<MT, NW>& dd_slot() {
+  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW> slot;
+  return slot;
+}
+
+template <int MT, int NW, int NR, bool kBf16Out>
+__global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* __restrict__ wq,
+                                                                const uint8_t* __restrict__ ws, int64_t n,
+                                                                int64_t k, const uint16_t* __restrict__ x,
+                                                                int64_t m, void* __restrict__ y) {
+  constexpr int RB = 16 * NW;                 // weight rows per block
+  constexpr int XPW = (MT + NW - 1) / NW;     // activation-row copies per wave per stage
+  constexpr int D = 4 + 1 + XPW;              // copies per wave per stage
+  static_assert(NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "ring depth / vmcnt range");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * RB;
+  const int rows_w = (int)min((int64_t)RB, n - n0);
+  const int64_t kq = k / 2, ks = k / 32, kx = k * 2;
+  const int nst = (int)(k / kDdK);
+
+  // zero rows (activation rows m..15 of the MFMA operand read them)
+  for (int i = tid; i < kDdXRowB / 16; i += 64 * NW) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *(u32x4*)(dd_slot<MT, NW, 0>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, 1 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, 2 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, 3 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+  }
+  __syncthreads();
+
+  // copies of stage s into ring slot B: 4 code instructions, 1 scale
+  // instruction, XPW activation instructions.  A stage past the end is
+  // clamped to the last one (a re-read from L2 into a slot nobody reads), so
+  // every step issues the same copies and waits for the same count, and the
+  // code between the copies and the reads has no branch.  Lane offsets are
+  // fixed for the whole k loop; a stage only moves the uniform bases.
+  unsigned offw[4], offx[XPW];
+  int xdst[XPW];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int row = 16 * wave + 4 * q + (lane >> 4);  // block row of this lane
+    const unsigned unit = (unsigned)((lane & 15) ^ (row & 15));
+    offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
+  }
+  const unsigned offs = (unsigned)min(16 * wave + (lane >> 2), rows_w - 1) * (unsigned)ks + 4u * (lane & 3);
+#pragma unroll
+  for (int j = 0; j < XPW; j++) {
+    const int xr = wave + NW * j;  // activation row of this copy (wave-uniform)
+    const bool real = xr < m;
+    offx[j] = real ? (unsigned)xr * (unsigned)kx + ((unsigned)(lane ^ (xr & 15)) << 4) : 0u;
+    xdst[j] = (real ? xr : MT + 1) * kDdXRowB;
+  }
+  const uint8_t* gw0 = wq + n0 * kq;
+  const uint8_t* gs0 = ws + n0 * ks;
+  auto issue = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
+    const int sc = min(s, nst - 1);
+    const uint8_t* gw = gw0 + (unsigned)sc * (unsigned)kDdRowB;
+#pragma unroll
+    for (int q = 0; q < 4; q++) gdma16(gw + offw[q], sl.w + (16 * wave + 4 * q) * kDdRowB);
+    gdma4(gs0 + (unsigned)sc * (unsigned)kDdScB + offs, sl.s + 16 * wave * kDdScB);
+    const uint8_t* gx = (const uint8_t*)x + (unsigned)sc * (unsigned)kDdXRowB;
+#pragma unroll
+    for (int j = 0; j < XPW; j++) gdma16(gx + offx[j], sl.x + xdst[j]);
+  };
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int wrow = 16 * wave + col;  // this lane's block weight row
+  const bool xreal = col < m;
+  auto compute = [&](auto slot_tag) {
+    constexpr int B = decltype(slot_tag)::value;
+    const DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
+    const uint8_t* xb = sl.x + (xreal ? col : MT) * kDdXRowB;
+    const int xsw = xreal ? col : 0;
+    const u32x4 sv = *(const u32x4*)(sl.s + wrow * kDdScB);
+    const unsigned svs[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const u32x4 cw = *(const u32x4*)(sl.w + wrow * kDdRowB + (((4 * i + g) ^ col) << 4));
+      const float scale = e8m0_as_scale((svs[i] >> (8 * g)) & 0xFFu);
+      const unsigned d[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bf16x8 xa = *(const bf16x8*)(xb + ((16 * i + ((4 * g + j) ^ xsw)) << 4));
+        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
+        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
+        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
+        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
+        const bf16x8 wf = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wf, acc, 0, 0, 0);
+      }
+    }
+  };
+
+  // one stage: wait for its copies (NR - 2 later stages may stay in
+  // flight), meet the other waves, refill the slot everyone finished in the
+  // previous stage, multiply.  Every step issues, so the count is constant
+  // and the code between the copies and the reads has no branch.
+  auto step = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    // this wave's copies of stage s have landed and its reads of the slot
+    // about to be refilled are complete (lgkmcnt(0)), then the barrier
+    constexpr int N = (NR - 2) * D;
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
+    if (s < nst) compute(slot_tag);
+  };
+
+  // prologue: stages 0 .. NR-2 in flight, then stage 0.  The loop below
+  // starts at the step that refills slot 0, so that the copies of one trip
+  // target the slots in the same order as the prologue's.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % NR>;
+  using I2 = std::integral_constant<int, 2 % NR>;
+  using I3 = std::integral_constant<int, 3 % NR>;
+  issue(I0{}, 0);
+  if (NR > 2) issue(I1{}, 1);
+  if (NR > 3) issue(I2{}, 2);
+  step(I0{}, 0);
+  for (int s = 1; s < nst; s += NR) {
+    step(I1{}, s);
+    if (NR > 2) step(I2{}, s + 1);
+    if (NR > 3) step(I3{}, s + 2);
+    step(I0{}, s + NR - 1);
+  }
+  gwait_vmcnt<0>();
+
+  // lane holds y[4g + i][n0 + wrow]
+  const int64_t nn = n0 + wrow;
+  if (nn < n) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t mm = 4 * g + i;
+      if (mm >= m) continue;
+      if (kBf16Out)
+        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(acc[i]);
+      else
+        ((float*)y)[mm * n + nn] = acc[i];
+    }
+  }
+}
+
+template <int MT, int NW, int NR>
+static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, int64_t n, int64_t k, const void* x, int64_t m,
+                              void* y, bool bf16_out, hipStream_t st) {
+  const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
+  if (bf16_out)
+    hipLaunchKernelGGL((k_w4a16_decode_dma<MT, NW, NR, true>), grid, dim3(64 * NW), 0, st, wq, ws, n, k,
+                       (const uint16_t*)x, m, y);
+  else
+    hipLaunchKernelGGL((k_w4a16_decode_dma<MT, NW, NR, false>), grid, dim3(64 * NW), 0, st, wq, ws, n, k,
+                       (const uint16_t*)x, m, y);
+}
+
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  if (!nv && m >= 5 && m <= 16) {
+  if (!nv && m >= 2 && m <= 16 && k % kDdK == 0 && k <= (1 << 24) && n >= 16 * 7 * 128) {
+    if (m <= 4)
+      launch_decode_dma<4, 7, 4>(wq, ws, n, k, x, m, y, bf16_out, st);
+    else
+      launch_decode_dma<16, 7, 3>(wq, ws, n, k, x, m, y, bf16_out, st);
+  } else if (!nv && m >= 5 && m <= 16) {
     const dim3 grid((unsigned)((n + 63) / 64));
     if (bf16_out)
       hipLaunchKernelGGL(k_w4a16_decode_mfma<true>, grid, dim3(256), 0, st, wq, ws, n, k, (const uint16_t*)x, m, y);

@@ -282,6 +282,18 @@ def test_gemv_ragged_shapes(n, k, m):
     mx_w4a16_case(w, x, f"w4a16 n={n} k={k} m={m}")
 
 
+# Shapes that reach the DMA-fed decode kernel (n >= 14336 rows, k a
+# multiple of 512, 2 <= m <= 16): one to eight 512-k stages against a three-
+# or four-slot ring, row tails that leave part of the last block empty, and
+# activation counts on both sides of the 4-row variant.
+@pytest.mark.parametrize("n,k,m", [(14336, 512, 2), (14373, 1024, 3), (14447, 1536, 4), (14400, 2048, 5),
+                                   (14336, 2560, 16), (15000, 1536, 12), (14336, 4096, 2)])
+def test_gemv_decode_dma_shapes(n, k, m):
+    w = laplace_bf16(n + 7 * k + m, n, k)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(100 + m).standard_normal((m, k)).astype(np.float32))
+    mx_w4a16_case(w, x, f"w4a16 dma n={n} k={k} m={m}")
+
+
 def test_gemv_one_hot_reproduces_weight_column():
     w = laplace_bf16(3, 64, 256)
     qo, so = oracle.mx_quantize(w)
