@@ -12,6 +12,8 @@
 // scale byte.  One lane's k range is therefore exactly one MXFP4 block, and
 // the stored codes are fed to the MFMA unchanged.  The 32 x 32 fp32 result
 // sits in lane l, column l % 32, rows 8*(r/4) + 4*(l/32) + r%4 of register r.
+#include <type_traits>
+
 #include "mxq_device.h"
 #include "mxq_launch.h"
 
@@ -311,15 +313,28 @@ __device__ __forceinline__ void interleave_reads_mfma() {
   }
 }
 
+// Ring slots: each stage buffer and each scale-pair buffer is its own LDS
+// variable, addressed only through compile-time slot indices, so the
+// compiler can see that the fragment reads of one slot do not touch the
+// slot whose copy is in flight (with one shared array it would wait for
+// every outstanding copy before the first read, serializing copy and math).
+template <int B>
+__device__ __forceinline__ uint8_t* w4_codes() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[kRStage];
+  return buf;
+}
+template <int B>
+__device__ __forceinline__ uint8_t* w4_scales() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[kRScale];
+  return buf;
+}
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
                                                       const uint8_t* __restrict__ as,
                                                       const uint8_t* __restrict__ bq,
                                                       const uint8_t* __restrict__ bs, int64_t m, int64_t n,
                                                       int64_t k, void* __restrict__ c) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][kRStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sring[2][kRScale];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, r32 = lane & 31;
@@ -337,37 +352,45 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
 
   const int64_t kq = k / 2, ks = k / 32;
-  const int nstages = (int)(k / 256);
+  const int nstages = (int)(k / 256);  // a multiple of 4 (k % 1024 == 0)
+  const int npairs = nstages / 2;
 
   // rows of this tile that exist (the last tile may be partial: its missing
   // rows re-read the last row and are never stored)
   const int rows_a = (int)min((int64_t)kBM, m - m0), rows_b = (int)min((int64_t)kBN, n - n0);
   const uint8_t* gsa = as + min(m0 + 64 * wave + lane, m - 1) * ks;
   const uint8_t* gsb = bs + min(n0 + 64 * wave + lane, n - 1) * ks;
+  // lane offsets of the 8 code copies per operand (fixed for the k loop)
+  unsigned offa[8], offb[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    // lane -> LDS row 64w + 8j + lane/8, physical unit lane%8, logical unit
+    // (lane%8) ^ ((row >> 1) & 7) = (lane%8) ^ ((4j + lane/16) & 7)
+    const int row = 64 * wave + 8 * j + (lane >> 3);
+    const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
+    offa[j] = (unsigned)min(row, rows_a - 1) * (unsigned)kq + cu16;
+    offb[j] = (unsigned)min(row, rows_b - 1) * (unsigned)kq + cu16;
+  }
 
-  // codes of stage s: 16 DMA instructions per wave; on even s also the
-  // scales of the pair (s, s+1): 2 more
-  auto issue = [&](int s, int buf) {
-    uint8_t* base = ring[buf];
-    // uniform 64-bit bases + 32-bit per-lane offsets (SGPR-base addressing)
-    const uint8_t* srcA = aq + m0 * kq + (int64_t)s * kSB;
-    const uint8_t* srcB = bq + n0 * kq + (int64_t)s * kSB;
+  // codes of stage s into code slot CB: 16 copies per wave (a stage past the
+  // end is clamped to the last one: a re-read into a slot nobody reads)
+  auto issue_codes = [&](auto cb_tag, int s) {
+    uint8_t* base = w4_codes<decltype(cb_tag)::value>();
+    const int sc = min(s, nstages - 1);
+    const uint8_t* srcA = aq + m0 * kq + (int64_t)sc * kSB;
+    const uint8_t* srcB = bq + n0 * kq + (int64_t)sc * kSB;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      // lane -> LDS row 64w + 8j + lane/8, physical unit lane%8, logical unit
-      // (lane%8) ^ ((row >> 1) & 7) = (lane%8) ^ ((4j + lane/16) & 7)
-      const int row = 64 * wave + 8 * j + (lane >> 3);
-      const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
-      const unsigned offa = (unsigned)min(row, rows_a - 1) * (unsigned)kq + cu16;
-      const unsigned offb = (unsigned)min(row, rows_b - 1) * (unsigned)kq + cu16;
-      dma16(srcA + offa, base + (64 * wave + 8 * j) * kSB);
-      dma16(srcB + offb, base + kBM * kSB + (64 * wave + 8 * j) * kSB);
+      dma16(srcA + offa[j], base + (64 * wave + 8 * j) * kSB);
+      dma16(srcB + offb[j], base + kBM * kSB + (64 * wave + 8 * j) * kSB);
     }
-    if ((s & 1) == 0) {
-      uint8_t* sbase = sring[(s >> 1) & 1];
-      dma16(gsa + (int64_t)s * 8, sbase + (64 * wave) * 16);
-      dma16(gsb + (int64_t)s * 8, sbase + kBM * 16 + (64 * wave) * 16);
-    }
+  };
+  // scales of stage pair p into scale slot SB: 16 B per row, 2 copies per wave
+  auto issue_scales = [&](auto sb_tag, int p) {
+    uint8_t* sbase = w4_scales<decltype(sb_tag)::value>();
+    const int pc = min(p, npairs - 1);
+    dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
+    dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * wave) * 16);
   };
 
   f32x16 acc[4][4];
@@ -379,16 +402,17 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   struct Frag {
     i32x4 a[4], b[4];
   };
-  // fragments of 64-k step kk (0..3) of the stage in buffer buf
+  // fragments of 64-k step kk (0..3) of the stage in code slot CB.
   // Fragment addresses factor: row = w*128 + i*32 + r32 has (row >> 1) & 7
   // == (r32 >> 1) & 7 for every i and for A and B alike, so one physical
   // unit per k step serves all eight fragments and i is an immediate offset.
   const int swz = (r32 >> 1) & 7;
   const int laneA = (wm * 128 + r32) * kSB, laneB = kBM * kSB + (wn * 128 + r32) * kSB;
-  auto read_frag = [&](int buf, int kk, Frag& f) {
+  auto read_frag = [&](auto cb_tag, int kk, Frag& f) {
+    const uint8_t* ring = w4_codes<decltype(cb_tag)::value>();
     const int unit16 = ((kk * 2 + half) ^ swz) << 4;
-    const uint8_t* pa = ring[buf] + laneA + unit16;
-    const uint8_t* pb = ring[buf] + laneB + unit16;
+    const uint8_t* pa = ring + laneA + unit16;
+    const uint8_t* pb = ring + laneB + unit16;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       f.a[i] = *(const i32x4*)(pa + i * 32 * kSB);
@@ -400,10 +424,10 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   struct Scales {
     unsigned a[4][2], b[4][2];
   };
-  // stage s's scale dwords: dwords 2(s&1), 2(s&1)+1 of the pair buffer
-  auto read_scales = [&](int s, Scales& sc) {
-    const unsigned* ss = (const unsigned*)sring[(s >> 1) & 1];
-    const int d0 = 2 * (s & 1);
+  // stage s's scale dwords: dwords 2(s&1), 2(s&1)+1 of the pair in slot SB
+  auto read_scales = [&](auto sb_tag, int odd, Scales& sc) {
+    const unsigned* ss = (const unsigned*)w4_scales<decltype(sb_tag)::value>();
+    const int d0 = 2 * odd;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int ra_row = wm * 128 + i * 32 + r32;
@@ -431,45 +455,62 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
       }
   };
 
-  // prologue
-  issue(0, 0);
-  issue(1, 1);  // nstages >= 2: k % 512 == 0
-  wait_vmcnt<16>();  // stage 0 (18 DMAs) landed; stage 1 (16) may be in flight
-  __builtin_amdgcn_s_barrier();
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
   Frag f0, f1;
   Scales sc;
-  read_scales(0, sc);
-  read_frag(0, 0, f0);
-
-  for (int s = 0; s < nstages; s++) {
-    const int buf = s & 1;
-    read_frag(buf, 1, f1);
+  // one stage s (S = s % 4): code slot S & 1, scale slot S >> 1.  Straight-
+  // line code: the copies, the waits and the reads of the next stage have
+  // no branch between them.
+  auto stage = [&](auto s_tag, int s) {
+    constexpr int S = decltype(s_tag)::value;
+    using CB = std::integral_constant<int, S & 1>;
+    using NB = std::integral_constant<int, (S + 1) & 1>;
+    using NSB = std::integral_constant<int, ((S + 1) >> 1) & 1>;
+    read_frag(CB{}, 1, f1);
     mma(f0, sc, 0);
     interleave_reads_mfma<2>();
-    read_frag(buf, 2, f0);
+    read_frag(CB{}, 2, f0);
     mma(f1, sc, 1);
     interleave_reads_mfma<2>();
-    read_frag(buf, 3, f1);
+    read_frag(CB{}, 3, f1);
     mma(f0, sc, 2);
     interleave_reads_mfma<2>();
-    // last k step: stage s+1 must be visible before its fragments are read,
-    // and this stage's buffer is refilled with stage s+2 once every wave has
-    // finished reading it
-    Scales scn;
-    const bool more = s + 1 < nstages;
-    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8));  // lgkmcnt(0): this wave's reads done
-    wait_vmcnt<0>();                                          // stage s+1 landed
+    // stage s+1 must be visible before its fragments are read, and this
+    // stage's slot is refilled with stage s+2 once every wave has finished
+    // reading it (this wave's reads: lgkmcnt(0); everyone's: the barrier)
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8));
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < nstages) issue(s + 2, buf);
-    if (more) {
-      read_scales(s + 1, scn);
-      read_frag(buf ^ 1, 0, f0);
-    }
+    // the copies go out right after the barrier (the scheduler would sink
+    // them to the end of the stage, shrinking the time they have to land)
+    __builtin_amdgcn_sched_barrier(0);
+    issue_codes(CB{}, s + 2);
+    if constexpr ((S & 1) == 0) issue_scales(std::integral_constant<int, ((S + 2) >> 1) & 1>{}, (s + 2) >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+    Scales scn;
+    read_scales(NSB{}, (S + 1) & 1, scn);
+    read_frag(NB{}, 0, f0);
     mma(f1, sc, 3);
     interleave_reads_mfma<3>();
-    if (more) sc = scn;
+    sc = scn;
+  };
+
+  // prologue: stages 0 and 1 and the scales of pair 0 in flight
+  issue_codes(C0{}, 0);
+  issue_scales(C0{}, 0);
+  issue_codes(C1{}, 1);
+  wait_vmcnt<16>();  // stage 0 (18 copies) landed; stage 1 (16) may be in flight
+  __builtin_amdgcn_s_barrier();
+  read_scales(C0{}, 0, sc);
+  read_frag(C0{}, 0, f0);
+  for (int s = 0; s < nstages; s += 4) {
+    stage(std::integral_constant<int, 0>{}, s);
+    stage(std::integral_constant<int, 1>{}, s + 1);
+    stage(std::integral_constant<int, 2>{}, s + 2);
+    stage(std::integral_constant<int, 3>{}, s + 3);
   }
-  wait_vmcnt<0>();  // no DMA may still target LDS when the block ends
+  wait_vmcnt<0>();  // no copy may still target LDS when the block ends
 
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -506,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
 
 hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  if (k % 512 == 0 && k >= 512) {
+  if (k % 1024 == 0 && k >= 1024) {
     const unsigned tiles = (unsigned)(((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
     if (bf16_out)
       hipLaunchKernelGGL(k_w4a4_ring<true>, dim3(tiles), dim3(256), 0, st, aq, as, bq, bs, m, n, k, c);
