@@ -433,10 +433,35 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void gdma16(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
 }
+// The same copy through a buffer resource (buffer_load_dwordx4 ... lds):
+// base and record count in SGPRs, a 32-bit per-lane offset and a uniform
+// per-stage offset.  The compiler tracks it as a plain vector-memory
+// operation, so LDS reads of other slots that follow it need not drain it.
+constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
 template <int N>
 __device__ __forceinline__ void gwait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One ring slot of the GEMM (activations and weight codes of one stage).
+// Every slot is its own LDS variable and is addressed only through
+// compile-time slot indices, so the compiler can tell that the reads of one
+// slot do not touch the slots whose copies are in flight.
+struct GSlot {
+  uint8_t x[kGXStage];
+  uint8_t w[kGWStage];
+};
+template <int B>
+__device__ __forceinline__ GSlot& g_slot() {
+  __shared__ __attribute__((aligned(1024))) GSlot slot;
+  return slot;
 }
 
 template <bool kNv, bool kBf16Out>
@@ -444,9 +469,6 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
                                                        const float* __restrict__ gscale, int64_t n, int64_t k,
                                                        const uint16_t* __restrict__ x, int64_t m,
                                                        void* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xring[kGRing][kGXStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t wring[kGRing][kGWStage];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, r32 = lane & 31;
@@ -469,23 +491,30 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   // stage s into ring slot b (near the end the stage index is clamped to the
   // last stage so every step issues the same number of loads; the copy lands
   // in the free slot and is never read)
-  auto issue = [&](int s, int b) {
-    uint8_t* xb = xring[b];
-    uint8_t* wb = wring[b];
-    const uint8_t* sx = (const uint8_t*)x + m0 * kx + (int64_t)s * 128;
+  // buffer resources of the tile's row panels; per-lane offsets fixed for
+  // the whole k loop, the stage moves the uniform offset only
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const uint8_t*)x + m0 * kx, (unsigned)(rows_x * kx));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * kq, (unsigned)(rows_w * kq));
+  unsigned offx[8], offw[2];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int row = 64 * wave + 8 * j + (lane >> 3);
-      const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
-      gdma16(sx + (unsigned)min(row, rows_x - 1) * (unsigned)kx + cu16, xb + (64 * wave + 8 * j) * 128);
-    }
-    const uint8_t* sw = wq + n0 * kq + (int64_t)s * 32;
+  for (int j = 0; j < 8; j++) {
+    const int row = 64 * wave + 8 * j + (lane >> 3);
+    const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
+    offx[j] = (unsigned)min(row, rows_x - 1) * (unsigned)kx + cu16;
+  }
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int row = 64 * wave + 32 * j + (lane >> 1);
-      const unsigned cu16 = (unsigned)(((lane & 1) ^ ((row >> 3) & 1)) << 4);
-      gdma16(sw + (unsigned)min(row, rows_w - 1) * (unsigned)kq + cu16, wb + (64 * wave + 32 * j) * 32);
-    }
+  for (int j = 0; j < 2; j++) {
+    const int row = 64 * wave + 32 * j + (lane >> 1);
+    const unsigned cu16 = (unsigned)(((lane & 1) ^ ((row >> 3) & 1)) << 4);
+    offw[j] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + cu16;
+  }
+  auto issue = [&](auto slot_tag, int s) {
+    uint8_t* xb = g_slot<decltype(slot_tag)::value>().x;
+    uint8_t* wb = g_slot<decltype(slot_tag)::value>().w;
+#pragma unroll
+    for (int j = 0; j < 8; j++) bdma16(rx, offx[j], (unsigned)s * 128u, xb + (64 * wave + 8 * j) * 128);
+#pragma unroll
+    for (int j = 0; j < 2; j++) bdma16(rw, offw[j], (unsigned)s * 32u, wb + (64 * wave + 32 * j) * 32);
   };
   // this lane's scale byte(s) for its four weight rows at stage s (global,
   // L2-resident): MXFP4 block 2s + half; NVFP4 blocks 4s + 2 half + {0, 1}
@@ -512,9 +541,9 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   const int laneX = (wm * 128 + r32) * 128;
   const int laneW = (wn * 128 + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
 
-  auto compute = [&](int s, const unsigned sc[4]) {
-    const uint8_t* xb = xring[s % kGRing];
-    const uint8_t* wb = wring[s % kGRing];
+  auto compute = [&](auto slot_tag, const unsigned sc[4]) {
+    const uint8_t* xb = g_slot<decltype(slot_tag)::value>().x;
+    const uint8_t* wb = g_slot<decltype(slot_tag)::value>().w;
     u32x4 wc[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
@@ -551,20 +580,42 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
     }
   };
 
-  // prologue: stages 0, 1 in flight
-  issue(0, 0);
-  issue(min(1, nstages - 1), 1);
+  // one stage s in ring slot B: fetch the next stage's scales, wait for
+  // stage s (stage s+1's 10 copies and the 4 scale loads may stay in
+  // flight), meet, refill the slot of stage s-1 with stage s+2 (clamped to
+  // the last stage near the end: the copy lands in a free slot), multiply.
+  // Slot indices are compile-time constants (the loop is unrolled by 3).
   unsigned sc_cur[4], sc_nxt[4];
-  load_scales(0, sc_cur);
-  for (int s = 0; s < nstages; s++) {
+  // (scheduling fences keep the scale loads and the copies where they are
+  // written: the scheduler would sink them next to their first use)
+  auto step = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
     load_scales(min(s + 1, nstages - 1), sc_nxt);
-    gwait_vmcnt<10 + 4>();  // stage s landed; stage s+1 and the 4 scale loads may be in flight
+    __builtin_amdgcn_sched_barrier(0);
+    gwait_vmcnt<10 + 4>();
     __builtin_amdgcn_s_barrier();  // no fence: the prefetched stages stay in flight
-    issue(min(s + kGRing - 1, nstages - 1), (s + kGRing - 1) % kGRing);
-    compute(s, sc_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(std::integral_constant<int, (B + kGRing - 1) % kGRing>{}, min(s + kGRing - 1, nstages - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(slot_tag, sc_cur);
 #pragma unroll
     for (int j = 0; j < 4; j++) sc_cur[j] = sc_nxt[j];
+  };
+  static_assert(kGRing == 3, "the stage loop is unrolled by the ring depth");
+  // prologue: stages 0, 1 in flight
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, min(1, nstages - 1));
+  load_scales(0, sc_cur);
+  // whole trips of three stages (no branch inside a trip), then up to two
+  int s = 0;
+  for (; s + 3 <= nstages; s += 3) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
   }
+  if (s < nstages) step(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nstages) step(std::integral_constant<int, 1>{}, s + 1);
   gwait_vmcnt<0>();
 
   const float st = kNv ? *gscale : 1.0f;
