@@ -541,43 +541,68 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   const int laneX = (wm * 128 + r32) * 128;
   const int laneW = (wn * 128 + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
 
+  // weight operands of k step kk from the stage's code chunks: MXFP4 with
+  // the scaled convert (exact bf16), NVFP4 as E4M3 * E2M1 in fp32 (exact,
+  // at most 6 significant bits) rounded to bf16 (exact)
+  auto dequant = [&](const u32x4 wc[4], int kk, const unsigned sc[4], bf16x8 wf[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const unsigned d = kk == 0 ? wc[j].x : kk == 1 ? wc[j].y : kk == 2 ? wc[j].z : wc[j].w;
+      if (!kNv) {
+        const float scale = e8m0_as_scale(sc[j] & 0xFFu);
+        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+        wf[j] = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      } else {
+        const float sb = e4m3_value(kk < 2 ? (sc[j] & 0xFFu) : ((sc[j] >> 8) & 0xFFu));
+        auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+        auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+        auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+        auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+        wf[j] = (bf16x8){(__bf16)(p0[0] * sb), (__bf16)(p0[1] * sb), (__bf16)(p1[0] * sb), (__bf16)(p1[1] * sb),
+                         (__bf16)(p2[0] * sb), (__bf16)(p2[1] * sb), (__bf16)(p3[0] * sb), (__bf16)(p3[1] * sb)};
+      }
+    }
+  };
+  auto read_x = [&](const uint8_t* xb, int kk, bf16x8 xf[4]) {
+    const int unit16 = ((4 * half + kk) ^ swz) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; i++) xf[i] = *(const bf16x8*)(xb + laneX + i * 32 * 128 + unit16);
+  };
+  // Software pipeline inside a stage (fixed by scheduling fences): the
+  // activation fragments of step kk+1 are read and the weight operands of
+  // step kk+1 are expanded while the 16 MFMAs of step kk run.
   auto compute = [&](auto slot_tag, const unsigned sc[4]) {
     const uint8_t* xb = g_slot<decltype(slot_tag)::value>().x;
     const uint8_t* wb = g_slot<decltype(slot_tag)::value>().w;
     u32x4 wc[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
+    bf16x8 xf[2][4], wf[2][4];
+    read_x(xb, 0, xf[0]);
+    dequant(wc, 0, sc, wf[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
-      bf16x8 xf[4], wf[4];
-      const int unit16 = ((4 * half + kk) ^ swz) << 4;
-#pragma unroll
-      for (int i = 0; i < 4; i++) xf[i] = *(const bf16x8*)(xb + laneX + i * 32 * 128 + unit16);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const unsigned d = kk == 0 ? wc[j].x : kk == 1 ? wc[j].y : kk == 2 ? wc[j].z : wc[j].w;
-        if (!kNv) {
-          const float scale = e8m0_as_scale(sc[j] & 0xFFu);
-          bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
-          bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
-          bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
-          bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
-          wf[j] = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-          const float sb = e4m3_value(kk < 2 ? (sc[j] & 0xFFu) : ((sc[j] >> 8) & 0xFFu));
-          auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
-          auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
-          auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-          auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-          wf[j] = (bf16x8){(__bf16)(p0[0] * sb), (__bf16)(p0[1] * sb), (__bf16)(p1[0] * sb), (__bf16)(p1[1] * sb),
-                           (__bf16)(p2[0] * sb), (__bf16)(p2[1] * sb), (__bf16)(p3[0] * sb), (__bf16)(p3[1] * sb)};
-        }
-      }
+      const int c = kk & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) read_x(xb, kk + 1, xf[c ^ 1]);
+      if (kk < 3) dequant(wc, kk + 1, sc, wf[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[c][j], xf[c][i], acc[i][j], 0, 0, 0);
+      // reads first, then each MFMA followed by a share of the expansion
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kNv ? 4 : 2, 0);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // one stage s in ring slot B: fetch the next stage's scales, wait for
