@@ -93,186 +93,21 @@ __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__
     }
 }
 
-// ---------------------------------------------------------------------------
-// Tiled kernel (k % 128 == 0).  Block tile 256 x 256, four waves of 128 x 128
-// (4 x 4 MFMAs of 32 x 32 per 64-wide k step), k advanced in stages of 128
-// (64 code bytes per row) through double-buffered LDS:
-//   * global -> registers -> LDS, 16 B per lane, four lanes per 64-B row
-//     segment; the next stage's loads are in flight while the current stage
-//     is multiplied;
-//   * LDS rows are 64 B; 16-byte unit u of row r is stored at u ^ ((r>>2)&3)
-//     so that the 16 rows read by one 16-lane group hit distinct banks;
-//   * E8M0 scales are staged as 4 bytes per row per stage; a lane whose k
-//     half is the upper one shifts its copy right by a byte, so op_sel 0 / 2
-//     pick the block of k step 0 / 1;
-//   * operands are swapped (B rows feed the instruction's A side), so a lane
-//     holds four consecutive output columns and stores them as one 8-byte
-//     bf16 write;
-//   * tiles are ordered per XCD: the blocks an XCD runs take a contiguous run
-//     of tile ids, grouped four tile rows deep for L2 reuse.
-constexpr int kBM = 256, kBN = 256, kStageBytes = 64;  // 128 k per stage
-
-template <bool kBf16Out>
-__global__ __launch_bounds__(256, 1) void k_w4a4_tiled(const uint8_t* __restrict__ aq,
-                                                       const uint8_t* __restrict__ as,
-                                                       const uint8_t* __restrict__ bq,
-                                                       const uint8_t* __restrict__ bs, int64_t m, int64_t n,
-                                                       int64_t k, void* __restrict__ c) {
-  __shared__ __attribute__((aligned(16))) uint8_t smA[2][kBM * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t smB[2][kBN * kStageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned ssA[2][kBM];
-  __shared__ __attribute__((aligned(16))) unsigned ssB[2][kBN];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int half = lane >> 5, r32 = lane & 31;
-
-  // ---- tile order: XCD-contiguous runs, grouped 4 tile rows deep
-  const int64_t tm_n = (m + kBM - 1) / kBM, tn_n = (n + kBN - 1) / kBN;
-  const int64_t tiles = tm_n * tn_n;
-  int64_t tid_lin = blockIdx.x;
-  if (tiles % 8 == 0) tid_lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
-  const int64_t group = 4;
-  const int64_t per_group = group * tn_n;
-  const int64_t g0 = (tid_lin / per_group) * group;
-  const int64_t gsz = (tm_n - g0) < group ? (tm_n - g0) : group;
-  const int64_t tm = g0 + (tid_lin % per_group) % gsz;
-  const int64_t tn = (tid_lin % per_group) / gsz;
-  const int64_t m0 = tm * kBM, n0 = tn * kBN;
-
-  const int64_t kq = k / 2, ks = k / 32;
-  const int nstages = (int)(k / 128);
-
-  // ---- global -> register staging: 4 + 4 code units and one scale dword each
-  u32x4 ra[4], rb[4];
-  unsigned rsa, rsb;
-  auto load_stage = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int u = tid + 256 * i;  // 16-B unit within the stage tile
-      const int row = u >> 2, cu = u & 3;
-      const int64_t ga = min(m0 + row, m - 1), gb = min(n0 + row, n - 1);
-      ra[i] = *(const u32x4*)(aq + ga * kq + (int64_t)s * kStageBytes + cu * 16);
-      rb[i] = *(const u32x4*)(bq + gb * kq + (int64_t)s * kStageBytes + cu * 16);
-    }
-    const int64_t ga = min(m0 + tid, m - 1), gb = min(n0 + tid, n - 1);
-    rsa = *(const unsigned*)(as + ga * ks + (int64_t)s * 4);
-    rsb = *(const unsigned*)(bs + gb * ks + (int64_t)s * 4);
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int u = tid + 256 * i;
-      const int row = u >> 2, cu = u & 3;
-      const int off = row * kStageBytes + ((cu ^ ((row >> 2) & 3)) << 4);
-      *(u32x4*)(&smA[buf][off]) = ra[i];
-      *(u32x4*)(&smB[buf][off]) = rb[i];
-    }
-    ssA[buf][tid] = rsa;
-    ssB[buf][tid] = rsb;
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  auto compute_stage = [&](int buf) {
-    unsigned sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const unsigned va = ssA[buf][wm * 128 + i * 32 + r32];
-      const unsigned vb = ssB[buf][wn * 128 + i * 32 + r32];
-      sa[i] = half ? (va >> 8) : va;
-      sb[i] = half ? (vb >> 8) : vb;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      const int unit = kk * 2 + half;
-      i32x8 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int ra_row = wm * 128 + i * 32 + r32;
-        const int rb_row = wn * 128 + i * 32 + r32;
-        i32x4 va = *(const i32x4*)(&smA[buf][ra_row * kStageBytes + ((unit ^ ((ra_row >> 2) & 3)) << 4)]);
-        i32x4 vb = *(const i32x4*)(&smB[buf][rb_row * kStageBytes + ((unit ^ ((rb_row >> 2) & 3)) << 4)]);
-        fa[i] = (i32x8){va.x, va.y, va.z, va.w, 0, 0, 0, 0};
-        fb[i] = (i32x8){vb.x, vb.y, vb.z, vb.w, 0, 0, 0, 0};
-      }
-      // C^T tile = B rows x A rows: instruction "A" = fb[j], "B" = fa[i]
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          if (kk == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 4, 4, 0, sb[j], 0,
-                                                                          sa[i]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 4, 4, 2, sb[j], 2,
-                                                                          sa[i]);
-        }
-    }
-  };
-
-  // steady state: one basic block per stage -- loads of stage s+1 in flight,
-  // stage s multiplied, then the loads land in the other buffer
-  for (int s = 0; s + 1 < nstages; s++) {
-    load_stage(s + 1);
-    __builtin_amdgcn_sched_barrier(0);  // issue the loads first
-    compute_stage(s & 1);
-    // keep the LDS writes (and their wait on the global loads) after the
-    // MFMAs, so the load latency hides behind this stage's math
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage((s + 1) & 1);
-    __syncthreads();
-  }
-  compute_stage((nstages - 1) & 1);
-
-  // ---- epilogue: lane holds C[m0 + wm*128 + 32i + r32][n0 + wn*128 + 32j + 8q + 4*half + (0..3)]
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int64_t row = m0 + wm * 128 + i * 32 + r32;
-    if (row >= m) continue;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + q * 8 + 4 * half;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
-                    v3 = acc[i][j][4 * q + 3];
-        if (col + 3 < n) {
-          if (kBf16Out) {
-            u32x2 o = {f32_to_bf16_rne(v0) | ((unsigned)f32_to_bf16_rne(v1) << 16),
-                       f32_to_bf16_rne(v2) | ((unsigned)f32_to_bf16_rne(v3) << 16)};
-            *(u32x2*)((uint16_t*)c + row * n + col) = o;
-          } else {
-            *(f32x4*)((float*)c + row * n + col) = (f32x4){v0, v1, v2, v3};
-          }
-        } else {
-          const float vv[4] = {v0, v1, v2, v3};
-          for (int e = 0; e < 4 && col + e < n; e++) {
-            if (kBf16Out)
-              ((uint16_t*)c)[row * n + col + e] = f32_to_bf16_rne(vv[e]);
-            else
-              ((float*)c)[row * n + col + e] = vv[e];
-          }
-        }
-      }
-    }
-  }
-}
+constexpr int kBM = 256, kBN = 256;  // block tile of the ring kernel
 
 // ---------------------------------------------------------------------------
-// Ring kernel (k % 512 == 0): the tiled kernel's math, fed by direct
+// Ring kernel (k % 1024 == 0).  Block tile 256 x 256; each wave multiplies
+// 32 x 32 blocks on v_mfma_scale_f32_32x32x64_f8f6f4 (one lane = 32 k = one
+// MX block = one E8M0 operand byte).  Operands are fed by direct
 // global -> LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
 // LDS base + 16 i), no staging registers.  A stage is 256 k = 128 code bytes
 // per row, so every request is a whole 128-B line (half-line requests ran at
-// roughly half the L2 throughput); two stages of 66 KiB ring in LDS.
+// roughly half the L2 throughput); two stages of 64 KiB ring in LDS.
+//   * Operands are swapped (B rows feed the instruction's A side), so a lane
+//     holds four consecutive output columns and stores them as one 8-byte
+//     bf16 write.
+//   * Tiles are ordered per XCD: the blocks an XCD runs take a contiguous
+//     run of tile ids, grouped four tile rows deep for L2 reuse.
 //   * LDS rows are 128 B; unit u (16 B) of row r sits at u ^ ((r >> 1) & 7),
 //     so the 16 rows one 16-lane group reads hit distinct banks.  The
 //     swizzle is applied on the global side: lane i of a DMA fills row i / 8,
@@ -303,13 +138,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Scheduling hint: R LDS reads, then 4 MFMAs, four times over.
-template <int R>
+// Scheduling hint: R LDS reads, then MG MFMAs, four times over.
+template <int R, int MG = 4>
 __device__ __forceinline__ void interleave_reads_mfma() {
 #pragma unroll
   for (int g = 0; g < 4; g++) {
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MG, 0);
   }
 }
 
@@ -329,14 +164,23 @@ __device__ __forceinline__ uint8_t* w4_scales() {
   return buf;
 }
 
-template <bool kBf16Out>
-__global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
-                                                      const uint8_t* __restrict__ as,
-                                                      const uint8_t* __restrict__ bq,
-                                                      const uint8_t* __restrict__ bs, int64_t m, int64_t n,
-                                                      int64_t k, void* __restrict__ c) {
+// NWV waves per block: 4 (a 2 x 2 grid of 128 x 128 wave tiles, one wave
+// per SIMD) or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's
+// MFMAs cover the other's waits).
+template <int NWV, bool kBf16Out>
+__global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
+                                                           const uint8_t* __restrict__ as,
+                                                           const uint8_t* __restrict__ bq,
+                                                           const uint8_t* __restrict__ bs, int64_t m, int64_t n,
+                                                           int64_t k, void* __restrict__ c) {
+  static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
+  constexpr int WNC = NWV / 2;        // wave columns
+  constexpr int WCOLS = kBN / WNC;    // output columns per wave
+  constexpr int JB = WCOLS / 32;      // B fragments per wave
+  constexpr int RPW = kBM / NWV;      // rows each wave copies per operand
+  constexpr int CJ = RPW / 8;         // copy instructions per operand per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNC, wn = wave % WNC;
   const int half = lane >> 5, r32 = lane & 31;
 
   const int64_t tm_n = (m + kBM - 1) / kBM, tn_n = (n + kBN - 1) / kBN;
@@ -358,71 +202,82 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   // rows of this tile that exist (the last tile may be partial: its missing
   // rows re-read the last row and are never stored)
   const int rows_a = (int)min((int64_t)kBM, m - m0), rows_b = (int)min((int64_t)kBN, n - n0);
-  const uint8_t* gsa = as + min(m0 + 64 * wave + lane, m - 1) * ks;
-  const uint8_t* gsb = bs + min(n0 + 64 * wave + lane, n - 1) * ks;
-  // lane offsets of the 8 code copies per operand (fixed for the k loop)
-  unsigned offa[8], offb[8];
+  // scale copies: 16 B per row per stage pair; with 4 waves each wave copies
+  // 64 rows of A and of B, with 8 waves waves 0-3 copy A and 4-7 copy B
+  const int srow = NWV == 4 ? 64 * wave + lane : 64 * (wave & 3) + lane;
+  const uint8_t* gsa = as + min(m0 + srow, m - 1) * ks;
+  const uint8_t* gsb = bs + min(n0 + srow, n - 1) * ks;
+  // lane offsets of the CJ code copies per operand (fixed for the k loop)
+  unsigned offa[CJ], offb[CJ];
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    // lane -> LDS row 64w + 8j + lane/8, physical unit lane%8, logical unit
+  for (int j = 0; j < CJ; j++) {
+    // lane -> LDS row RPW w + 8j + lane/8, physical unit lane%8, logical unit
     // (lane%8) ^ ((row >> 1) & 7) = (lane%8) ^ ((4j + lane/16) & 7)
-    const int row = 64 * wave + 8 * j + (lane >> 3);
+    const int row = RPW * wave + 8 * j + (lane >> 3);
     const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
     offa[j] = (unsigned)min(row, rows_a - 1) * (unsigned)kq + cu16;
     offb[j] = (unsigned)min(row, rows_b - 1) * (unsigned)kq + cu16;
   }
 
-  // codes of stage s into code slot CB: 16 copies per wave (a stage past the
-  // end is clamped to the last one: a re-read into a slot nobody reads)
+  // codes of stage s into code slot CB: 2 CJ copies per wave (a stage past
+  // the end is clamped to the last one: a re-read into a slot nobody reads)
   auto issue_codes = [&](auto cb_tag, int s) {
     uint8_t* base = w4_codes<decltype(cb_tag)::value>();
     const int sc = min(s, nstages - 1);
     const uint8_t* srcA = aq + m0 * kq + (int64_t)sc * kSB;
     const uint8_t* srcB = bq + n0 * kq + (int64_t)sc * kSB;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      dma16(srcA + offa[j], base + (64 * wave + 8 * j) * kSB);
-      dma16(srcB + offb[j], base + kBM * kSB + (64 * wave + 8 * j) * kSB);
+    for (int j = 0; j < CJ; j++) {
+      dma16(srcA + offa[j], base + (RPW * wave + 8 * j) * kSB);
+      dma16(srcB + offb[j], base + kBM * kSB + (RPW * wave + 8 * j) * kSB);
     }
   };
-  // scales of stage pair p into scale slot SB: 16 B per row, 2 copies per wave
+  // scales of stage pair p into scale slot SB: 16 B per row (2 copies per
+  // wave with 4 waves, 1 with 8)
   auto issue_scales = [&](auto sb_tag, int p) {
     uint8_t* sbase = w4_scales<decltype(sb_tag)::value>();
     const int pc = min(p, npairs - 1);
-    dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
-    dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * wave) * 16);
+    if (NWV == 4) {
+      dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
+      dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * wave) * 16);
+    } else if (wave < 4) {
+      dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
+    } else {
+      dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * (wave - 4)) * 16);
+    }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+    for (int j = 0; j < JB; j++) acc[i][j] = (f32x16){};
 
   struct Frag {
-    i32x4 a[4], b[4];
+    i32x4 a[4], b[JB];
   };
   // fragments of 64-k step kk (0..3) of the stage in code slot CB.
   // Fragment addresses factor: row = w*128 + i*32 + r32 has (row >> 1) & 7
   // == (r32 >> 1) & 7 for every i and for A and B alike, so one physical
   // unit per k step serves all eight fragments and i is an immediate offset.
   const int swz = (r32 >> 1) & 7;
-  const int laneA = (wm * 128 + r32) * kSB, laneB = kBM * kSB + (wn * 128 + r32) * kSB;
+  const int laneA = (wm * 128 + r32) * kSB, laneB = kBM * kSB + (wn * WCOLS + r32) * kSB;
   auto read_frag = [&](auto cb_tag, int kk, Frag& f) {
     const uint8_t* ring = w4_codes<decltype(cb_tag)::value>();
     const int unit16 = ((kk * 2 + half) ^ swz) << 4;
     const uint8_t* pa = ring + laneA + unit16;
     const uint8_t* pb = ring + laneB + unit16;
+    // B fragments first: the first MFMAs of a step need every B fragment
+    // but only the first A fragment (the MFMA order is A-outer, B-inner)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      f.a[i] = *(const i32x4*)(pa + i * 32 * kSB);
-      f.b[i] = *(const i32x4*)(pb + i * 32 * kSB);
-    }
+    for (int j = 0; j < JB; j++) f.b[j] = *(const i32x4*)(pb + j * 32 * kSB);
+#pragma unroll
+    for (int i = 0; i < 4; i++) f.a[i] = *(const i32x4*)(pa + i * 32 * kSB);
   };
   // scale dwords of this lane's rows (dword d = blocks 4d..4d+3 of the stage),
   // pre-shifted for the lane's k half
   struct Scales {
-    unsigned a[4][2], b[4][2];
+    unsigned a[4][2], b[JB][2];
   };
   // stage s's scale dwords: dwords 2(s&1), 2(s&1)+1 of the pair in slot SB
   auto read_scales = [&](auto sb_tag, int odd, Scales& sc) {
@@ -431,12 +286,15 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int ra_row = wm * 128 + i * 32 + r32;
-      const int rb_row = wn * 128 + i * 32 + r32;
+      const int rb_row = wn * WCOLS + i * 32 + r32;
 #pragma unroll
       for (int d = 0; d < 2; d++) {
-        const unsigned va = ss[ra_row * 4 + d0 + d], vb = ss[kBM * 4 + rb_row * 4 + d0 + d];
+        const unsigned va = ss[ra_row * 4 + d0 + d];
         sc.a[i][d] = half ? (va >> 8) : va;
-        sc.b[i][d] = half ? (vb >> 8) : vb;
+        if (i < JB) {
+          const unsigned vb = ss[kBM * 4 + rb_row * 4 + d0 + d];
+          sc.b[i][d] = half ? (vb >> 8) : vb;
+        }
       }
     }
   };
@@ -444,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+      for (int j = 0; j < JB; j++) {
         const i32x8 fa = {f.a[i].x, f.a[i].y, f.a[i].z, f.a[i].w, 0, 0, 0, 0};
         const i32x8 fb = {f.b[j].x, f.b[j].y, f.b[j].z, f.b[j].w, 0, 0, 0, 0};
         const unsigned sa = sc.a[i][kk >> 1], sb = sc.b[j][kk >> 1];
@@ -467,15 +325,17 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
     using CB = std::integral_constant<int, S & 1>;
     using NB = std::integral_constant<int, (S + 1) & 1>;
     using NSB = std::integral_constant<int, ((S + 1) >> 1) & 1>;
+    // reads per k step: 4 + JB fragments; MFMAs: 4 JB
+    constexpr int RG = (4 + JB + 3) / 4, MG = JB;
     read_frag(CB{}, 1, f1);
     mma(f0, sc, 0);
-    interleave_reads_mfma<2>();
+    interleave_reads_mfma<RG, MG>();
     read_frag(CB{}, 2, f0);
     mma(f1, sc, 1);
-    interleave_reads_mfma<2>();
+    interleave_reads_mfma<RG, MG>();
     read_frag(CB{}, 3, f1);
     mma(f0, sc, 2);
-    interleave_reads_mfma<2>();
+    interleave_reads_mfma<RG, MG>();
     // stage s+1 must be visible before its fragments are read, and this
     // stage's slot is refilled with stage s+2 once every wave has finished
     // reading it (this wave's reads: lgkmcnt(0); everyone's: the barrier)
@@ -492,7 +352,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
     read_scales(NSB{}, (S + 1) & 1, scn);
     read_frag(NB{}, 0, f0);
     mma(f1, sc, 3);
-    interleave_reads_mfma<3>();
+    interleave_reads_mfma<RG + 1, MG>();
     sc = scn;
   };
 
@@ -500,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   issue_codes(C0{}, 0);
   issue_scales(C0{}, 0);
   issue_codes(C1{}, 1);
-  wait_vmcnt<16>();  // stage 0 (18 copies) landed; stage 1 (16) may be in flight
+  wait_vmcnt<2 * CJ>();  // stage 0 and the scales landed; stage 1 (2 CJ copies) may be in flight
   __builtin_amdgcn_s_barrier();
   read_scales(C0{}, 0, sc);
   read_frag(C0{}, 0, f0);
@@ -517,10 +377,10 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
     const int64_t row = m0 + wm * 128 + i * 32 + r32;
     if (row >= m) continue;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < JB; j++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + q * 8 + 4 * half;
+        const int64_t col = n0 + wn * WCOLS + j * 32 + q * 8 + 4 * half;
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
                     v3 = acc[i][j][4 * q + 3];
         if (col + 3 < n) {
@@ -545,14 +405,21 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_ring(const uint8_t* __restrict_
   }
 }
 
+#ifndef MXQ_W4A4_RING_WAVES
+#define MXQ_W4A4_RING_WAVES 8
+#endif
+constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
+
 hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
   if (k % 1024 == 0 && k >= 1024) {
     const unsigned tiles = (unsigned)(((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
     if (bf16_out)
-      hipLaunchKernelGGL(k_w4a4_ring<true>, dim3(tiles), dim3(256), 0, st, aq, as, bq, bs, m, n, k, c);
+      hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, true>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs, m,
+                         n, k, c);
     else
-      hipLaunchKernelGGL(k_w4a4_ring<false>, dim3(tiles), dim3(256), 0, st, aq, as, bq, bs, m, n, k, c);
+      hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, false>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs,
+                         m, n, k, c);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));

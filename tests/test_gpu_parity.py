@@ -391,7 +391,8 @@ def w4a4_case(a_np, b_np, what, dts=(torch.float32, torch.bfloat16)):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (31, 33, 64), (70, 90, 160), (128, 128, 256), (200, 130, 1056),
                                    (257, 129, 96), (1, 1, 128), (300, 200, 384), (513, 257, 1280),
-                                   (256, 512, 2048), (1, 1, 512), (300, 700, 1024), (520, 260, 1536)])
+                                   (256, 512, 2048), (1, 1, 512), (300, 700, 1024), (520, 260, 1536),
+                                   (777, 1025, 4096), (1, 257, 3072), (513, 1, 1024)])
 def test_w4a4_ragged(m, n, k):
     rng = np.random.default_rng(m * n + k)
     a = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
