@@ -55,6 +55,12 @@ __device__ __forceinline__ float e8m0_as_scale(unsigned code) {
   return __uint_as_float(code << 23);
 }
 
+// 2^(code - 127) as an fp32 value for arithmetic (code 0 is the subnormal
+// 2^-127, which e8m0_as_scale cannot express as a plain multiplier).
+__device__ __forceinline__ float e8m0_value(unsigned code) {
+  return code ? __uint_as_float(code << 23) : 0x1p-127f;
+}
+
 // E4M3 (OCP FP8) value of a code: S EEEE MMM, bias 7, subnormals for
 // E = 0, and S 1111 111 is NaN.
 __device__ __forceinline__ float e4m3_value(unsigned c) {

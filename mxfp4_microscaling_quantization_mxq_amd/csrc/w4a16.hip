@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
             float p = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; i++) p = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p, false);
-            acc = __builtin_fmaf(p, e8m0_as_scale(sc[u] & 0xFFu), acc);
+            acc = __builtin_fmaf(p, e8m0_value(sc[u] & 0xFFu), acc);
           } else {
             float p0 = 0.f, p1 = 0.f;
 #pragma unroll
@@ -728,6 +728,12 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //   * One s_barrier per stage (after the wave's own copies of stage s have
 //     landed) makes the other waves' activation copies visible and frees the
 //     ring slot for the copy of stage s + NR - 1.
+//   * Blocks start their k loop at staggered stages: block b walks the
+//     stages from (b / 8) mod nst on, so the blocks resident at one time
+//     (dispatched round robin over the eight XCDs) read rows at different
+//     column offsets instead of all at the same one (about 10 % faster on
+//     a 28672 x 8192 weight).  The k order of a block's sum changes with
+//     its rotation; the result is still one fixed order per output row.
 constexpr int kDdK = 512;             // k per stage
 constexpr int kDdRowB = kDdK / 2;     // code bytes per row per stage
 constexpr int kDdScB = kDdK / 32;     // scale bytes per row per stage
@@ -769,6 +775,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = k / 32, kx = k * 2;
   const int nst = (int)(k / kDdK);
+  const int rot = (int)((blockIdx.x / 8) % (unsigned)nst);
 
   // zero rows (activation rows m..15 of the MFMA operand read them)
   for (int i = tid; i < kDdXRowB / 16; i += 64 * NW) {
@@ -807,7 +814,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
     DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
-    const int sc = min(s, nst - 1);
+    const int sl0 = min(s, nst - 1);
+    const int sc = sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst;
     const uint8_t* gw = gw0 + (unsigned)sc * (unsigned)kDdRowB;
 #pragma unroll
     for (int q = 0; q < 4; q++) gdma16(gw + offw[q], sl.w + (16 * wave + 4 * q) * kDdRowB);
@@ -910,7 +918,7 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   if (!nv && m >= 2 && m <= 16 && k % kDdK == 0 && k <= (1 << 24) && n >= 16 * 7 * 128) {
     if (m <= 4)
-      launch_decode_dma<4, 7, 4>(wq, ws, n, k, x, m, y, bf16_out, st);
+      launch_decode_dma<4, 7, 3>(wq, ws, n, k, x, m, y, bf16_out, st);
     else
       launch_decode_dma<16, 7, 3>(wq, ws, n, k, x, m, y, bf16_out, st);
   } else if (!nv && m >= 5 && m <= 16) {

@@ -294,6 +294,23 @@ def test_gemv_decode_dma_shapes(n, k, m):
     mx_w4a16_case(w, x, f"w4a16 dma n={n} k={k} m={m}")
 
 
+@pytest.mark.parametrize("n,k,m", [(70, 256, 1), (33, 4096, 3), (14336, 512, 4), (14336, 1024, 16), (40, 320, 7),
+                                   (64, 512, 130)])
+def test_gemv_scale_code_zero_blocks(n, k, m):
+    """Blocks with E8M0 code 0 (2^-127) and non-zero elements: what the
+    quantizer emits for a block whose largest magnitude is below 2^-125.
+    Large activations (~2^120) bring the products back to ordinary sizes, so
+    a kernel that drops or flushes 2^-127 fails the bound by a wide margin."""
+    rng = np.random.default_rng(n + k + m)
+    qo = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    so = rng.choice(np.array([0, 0, 0, 1, 2, 3], dtype=np.uint8), size=(n, k // 32))
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * 2.0 ** 120).astype(np.float32))
+    yref, S = oracle.gemm_nt(oracle.to_f64(x), oracle.mx_dequantize(qo, so))
+    for dt in (torch.float32, torch.bfloat16):
+        y = host(mxq.gemv_w4a16(dev(qo), dev(so), dev(x), dt))
+        check_product(y, yref, S, dt == torch.bfloat16, f"scale-0 blocks n={n} k={k} m={m} {dt}")
+
+
 def test_gemv_one_hot_reproduces_weight_column():
     w = laplace_bf16(3, 64, 256)
     qo, so = oracle.mx_quantize(w)
