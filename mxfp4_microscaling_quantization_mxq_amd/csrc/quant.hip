@@ -100,36 +100,45 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restric
 
 // ---------------------------------------------------------------- NVFP4
 
-// Tensor amax [infra-guide sec. 2: s = max|x| / F_max].  The running max is
-// kept as fp32 magnitude bits in *g (cleared by k_nv_clear first); an
-// integer atomic max is exact and order-independent.
-__global__ void k_nv_clear(unsigned* g) { *g = 0u; }
+// Tensor amax [infra-guide sec. 2: s = max|x| / F_max], in two steps with
+// no atomics: every block of k_nv_amax writes the largest magnitude of its
+// grid-stride share (as fp32 bits; non-negative floats order like their
+// bits) to part[block], then one block of k_nv_scale folds the partials and
+// writes s_t.  part is the caller's code buffer, which the quantize pass
+// overwrites afterwards in stream order.  (One same-address device-scope
+// atomic per block cost about 8 us per call here: those atomics serialize
+// at the memory side.)
+constexpr int kAmaxU = 8;  // 16-byte loads in flight per lane
 
 template <bool kBf16In>
-__global__ __launch_bounds__(512) void k_nv_amax(const u32x4* __restrict__ x, int64_t nvec,
-                                                 unsigned* __restrict__ g) {
-  __shared__ unsigned wmax[8];
+__global__ __launch_bounds__(256) void k_nv_amax(const u32x4* __restrict__ x, int64_t nvec,
+                                                 unsigned* __restrict__ part) {
+  __shared__ unsigned wmax[4];
   unsigned m = 0;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    u32x4 v = __builtin_nontemporal_load(&x[i]);
-    if (kBf16In) {
-      unsigned h = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
-      m = max(m, max(h & 0xFFFFu, h >> 16) << 16);  // as fp32 bits
-    } else {
-      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+  const int64_t stride = (int64_t)gridDim.x * 256 * kAmaxU;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kAmaxU + threadIdx.x; base - threadIdx.x < nvec;
+       base += stride) {
+    u32x4 v[kAmaxU];
+#pragma unroll
+    for (int u = 0; u < kAmaxU; u++) {
+      const int64_t i = base + u * 256;
+      v[u] = i < nvec ? __builtin_nontemporal_load(&x[i]) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxU; u++) {
+      if (kBf16In) {
+        unsigned h = bf16x2_absmax_bits(bf16x2_absmax_bits(v[u].x, v[u].y), bf16x2_absmax_bits(v[u].z, v[u].w));
+        m = max(m, max(h & 0xFFFFu, h >> 16) << 16);  // as fp32 bits
+      } else {
+        m = max(m, max(max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu),
+                       max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu)));
+      }
     }
   }
-  // wave, then block reduction; one atomic per block (same-address atomics
-  // serialize in L2, so their number is kept to the grid size)
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned b = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); w++) b = max(b, wmax[w]);
-    if (b) atomicMax(g, b);
-  }
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
 }
 
 // s_t from the tensor amax: fl32(amax / 2688), or 1 for an all-zero tensor.
@@ -137,21 +146,43 @@ __device__ __forceinline__ float nv_tensor_scale(float amax) {
   return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 2688.0f);
 }
 
-// Turns the amax bits left in *g into the tensor scale (one thread).
-__global__ void k_nv_finalize(unsigned* g) { *(float*)g = nv_tensor_scale(__uint_as_float(*g)); }
+// One block: the largest of np partials, turned into s_t at *g.
+__global__ __launch_bounds__(256) void k_nv_scale(const unsigned* __restrict__ part, int np, float* __restrict__ g) {
+  __shared__ unsigned wmax[4];
+  unsigned m = 0;
+  for (int i = threadIdx.x; i < np; i += 256) m = max(m, part[i]);
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *g = nv_tensor_scale(__uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))));
+}
+
+// |x| / d rounded to nearest even (fp32), for d >= 2^-100 and |x| / d <= 2^100:
+// y = RN(1/d) (one IEEE division per block), q0 = RN(|x| y), then two
+// residual corrections r = |x| - d q (exact with an fma) and q += r y.
+// After the first correction q is within one ulp of |x| / d; with y
+// correctly rounded, the second correction returns the correctly rounded
+// quotient (Markstein's theorem on fma-based division).  Quotients below
+// 2^-3 may come out inexact, but every one of them still encodes to code 0.
+__device__ __forceinline__ float div_by_block_scale(float ax, float d, float y) {
+  float q = ax * y;
+  float r = __builtin_fmaf(-d, q, ax);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-d, q, ax);
+  return __builtin_fmaf(r, y, q);
+}
 
 // One lane = 8 consecutive elements, a pair of lanes = one 16-element block
 // [infra-guide sec. 4.1: 16 E2M1 + one E4M3, times the FP32 tensor scale].
 // fp32 order: t = fl(6 s_t); s_b = E4M3(fl(amax_b / t));
-// d = fl(s_t * s_b); q_i = E2M1_rne(fl(x_i / d)) with IEEE division.
+// d = fl(s_t * s_b); q_i = E2M1_rne(fl(x_i / d)), the quotient rounded once.
 template <bool kBf16In>
-__global__ __launch_bounds__(256) void k_nv_quantize(const u32x4* __restrict__ x,
-                                                     const unsigned* __restrict__ g,
-                                                     int amax_mode, unsigned* __restrict__ q,
-                                                     uint8_t* __restrict__ s, int64_t nlanes) {
+__global__ __launch_bounds__(256) void k_nv_quantize(const u32x4* __restrict__ x, const float* __restrict__ g,
+                                                     unsigned* __restrict__ q, uint8_t* __restrict__ s,
+                                                     int64_t nlanes) {
   int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nlanes) return;  // nlanes is even: pairs stay whole
-  float st = amax_mode ? nv_tensor_scale(__uint_as_float(*g)) : __uint_as_float(*g);
+  const float st = *g;
   float xs[8];
   unsigned m;
   if (kBf16In) {
@@ -181,10 +212,20 @@ __global__ __launch_bounds__(256) void k_nv_quantize(const u32x4* __restrict__ x
 #pragma unroll
     for (int i = 0; i < 8; i++) out |= (__float_as_uint(xs[i]) >> 31) << (3 + 4 * i);
   } else {
-    float d = st * sbv;
+    const float d = st * sbv;
     float v[8];
+    if (d >= 0x1p-100f && __uint_as_float(m) <= d * 0x1p100f) {
+      const float y = __fdiv_rn(1.0f, d);
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = __fdiv_rn(xs[i], d);
+      for (int i = 0; i < 8; i++) {
+        const unsigned xb = __float_as_uint(xs[i]);
+        const float aq = div_by_block_scale(__uint_as_float(xb & 0x7FFFFFFFu), d, y);
+        v[i] = __uint_as_float(__float_as_uint(aq) | (xb & 0x80000000u));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = __fdiv_rn(xs[i], d);
+    }
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], 1.0f, 0);
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], 1.0f, 1);
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], 1.0f, 2);
@@ -265,24 +306,24 @@ hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
                               bool compute_gscale, uint8_t* q, uint8_t* s, hipStream_t st) {
   int64_t n = rows * k;
   int64_t nlanes = n / 8;
-  unsigned* g = (unsigned*)gscale;
   if (compute_gscale) {
-    hipLaunchKernelGGL(k_nv_clear, dim3(1), dim3(1), 0, st, g);
-    int64_t nvec = bf16 ? n / 8 : n / 4;
-    unsigned blocks = (unsigned)std::min<int64_t>(grid_for(nvec, 512), 256);
+    // partials go to the code buffer (rows * k / 2 bytes, at least 8)
+    const int64_t nvec = bf16 ? n / 8 : n / 4;
+    const int64_t want = (nvec + 256 * kAmaxU - 1) / (256 * kAmaxU);
+    const int np = (int)std::max<int64_t>(1, std::min<int64_t>({want, 2048, n / 8}));
+    unsigned* part = (unsigned*)q;
     if (bf16)
-      hipLaunchKernelGGL(k_nv_amax<true>, dim3(blocks), dim3(512), 0, st, (const u32x4*)x, nvec, g);
+      hipLaunchKernelGGL(k_nv_amax<true>, dim3(np), dim3(256), 0, st, (const u32x4*)x, nvec, part);
     else
-      hipLaunchKernelGGL(k_nv_amax<false>, dim3(blocks), dim3(512), 0, st, (const u32x4*)x, nvec, g);
+      hipLaunchKernelGGL(k_nv_amax<false>, dim3(np), dim3(256), 0, st, (const u32x4*)x, nvec, part);
+    hipLaunchKernelGGL(k_nv_scale, dim3(1), dim3(256), 0, st, (const unsigned*)part, np, gscale);
   }
-  int mode = compute_gscale ? 1 : 0;
   if (bf16)
     hipLaunchKernelGGL(k_nv_quantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
-                       (const unsigned*)g, mode, (unsigned*)q, s, nlanes);
+                       (const float*)gscale, (unsigned*)q, s, nlanes);
   else
     hipLaunchKernelGGL(k_nv_quantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
-                       (const unsigned*)g, mode, (unsigned*)q, s, nlanes);
-  if (compute_gscale) hipLaunchKernelGGL(k_nv_finalize, dim3(1), dim3(1), 0, st, g);
+                       (const float*)gscale, (unsigned*)q, s, nlanes);
   return hipGetLastError();
 }
 

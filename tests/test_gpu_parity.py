@@ -217,6 +217,39 @@ def test_nv_quantize_e4m3_midpoints():
     assert_nv(x, float(st), "e4m3 midpoints")
 
 
+@pytest.mark.parametrize("st", [1.0, 0.7231445, 3.1e-9, 2.7e12, 1e-33])
+def test_nv_quantize_quotients_near_e2m1_boundaries(st):
+    """Elements placed within a few ulps of (E2M1 midpoint) * d for the block
+    divisor d = fl(s_t * s_b): the quotient x / d decides the code by its
+    last bit there, so any error in the division shows up as a code
+    mismatch.  Every positive finite E4M3 block scale is used, with a given
+    (static) tensor scale s_t."""
+    st = np.float32(st)
+    six_st = np.float32(6.0) * st
+    rng = np.random.default_rng(int(st * 1000) % 9973)
+    codes = np.arange(1, 127)
+    nblk = 8 * len(codes)
+    x = np.zeros((nblk, 16), dtype=np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.125, 5.999], dtype=np.float64)
+    for b in range(nblk):
+        e = oracle.e4m3_decode(int(codes[b % len(codes)]))
+        amax = np.float32(np.float32(e) * six_st)  # block amax -> s_b near e
+        x[b, 0] = amax
+        x[b, 1] = -amax
+    _, so, _ = oracle.nv_quantize(x, float(st))
+    for b in range(nblk):
+        sb = np.float32(oracle.e4m3_decode(int(so[b, 0])))
+        d = np.float32(st * sb)
+        for j in range(2, 16):
+            t = np.float32(mids[rng.integers(len(mids))] * float(d))
+            t = np.nextafter(t, np.float32(np.inf) if rng.integers(2) else np.float32(0.0))
+            for _ in range(int(rng.integers(0, 3))):
+                t = np.nextafter(t, np.float32(np.inf) if rng.integers(2) else np.float32(0.0))
+            t = min(t, np.abs(x[b, 0]))  # keep the block amax (and s_b) unchanged
+            x[b, j] = -t if rng.integers(2) else t
+    assert_nv(x.reshape(-1, 64), float(st), f"quotients near E2M1 boundaries, s_t={st}")
+
+
 def test_nv_zero_tensor_and_zero_blocks():
     x = np.zeros((4, 64), dtype=np.float32)
     x[1, 16:32] = -0.0
