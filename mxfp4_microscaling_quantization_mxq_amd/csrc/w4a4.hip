@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
     // stage s+1 must be visible before its fragments are read, and this
     // stage's slot is refilled with stage s+2 once every wave has finished
     // reading it (this wave's reads: lgkmcnt(0); everyone's: the barrier)
-    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     // the copies go out right after the barrier (the scheduler would sink
