@@ -73,6 +73,9 @@ def _load():
     lib.or_nv_dequantize.argtypes = [P, P, ctypes.c_float, I64, I64, P]
     lib.or_gemm_nt.argtypes = [P, P, I64, I64, I64, P, P]
     lib.or_metrics.argtypes = [P, P, I64, P, P]
+    lib.or_hadamard_norm.argtypes = [I]
+    lib.or_hadamard_norm.restype = ctypes.c_float
+    lib.or_hadamard_rotate.argtypes = [P, I, I64, I64, I, P]
     _lib = lib
     return lib
 
@@ -180,6 +183,31 @@ def nv_dequantize(q: np.ndarray, s: np.ndarray, gscale: float) -> np.ndarray:
     y = np.empty((rows, k), dtype=np.float64)
     _load().or_nv_dequantize(_ptr(q), _ptr(s), float(np.float32(gscale)), rows, k, _ptr(y))
     return y
+
+
+HADAMARD_SIZES = (16, 32, 64, 128)
+
+
+def hadamard_norm(hk: int) -> float:
+    """The fp32 factor 1/sqrt(hk) of the orthonormal block Hadamard."""
+    return float(_load().or_hadamard_norm(int(hk)))
+
+
+def hadamard_rotate(x: np.ndarray, hk: int) -> np.ndarray:
+    """x[rows][k] -> fp32 x rotated block by block along k with the
+    orthonormal Sylvester Hadamard H_hk, in the fixed fp32 butterfly order
+    [TransFP4 page sec. 2.3 eq. (2); FP4 analysis page sec. 3.2.3]."""
+    x, dt = _as_input(x)
+    rows, k = x.shape
+    assert hk in HADAMARD_SIZES and k % hk == 0
+    y = np.empty((rows, k), dtype=np.float32)
+    _load().or_hadamard_rotate(_ptr(x), dt, rows, k, int(hk), _ptr(y))
+    return y
+
+
+def mx_quantize_hadamard(x: np.ndarray, hk: int = 32):
+    """Rotated MXFP4: MXFP4 codes and scales of hadamard_rotate(x, hk)."""
+    return mx_quantize(hadamard_rotate(x, hk))
 
 
 def gemm_nt(a: np.ndarray, b: np.ndarray):

@@ -17,6 +17,9 @@
  *                optimization ch. 4), sec. 1.1, 1.2, 2, 3.1, 3.3, 4.1.
  *   [GPTOSS]     gpt-oss MXFP4 repost (juejin.cn post 7539732578421833769),
  *                section "MXFP4" with the four-value worked example.
+ *   [ANALYSIS]   "FP4 quantization analysis: MXFP4 and NVFP4 compared, in
+ *                practice" (jsqmd.com news), sec. 3.2.3 "fused online
+ *                rotation" (block-diagonal Hadamard H_k, k in 16..128).
  *
  * Precision discipline: every MXFP4 decision is exact (power-of-two scaling
  * of a float in double, then nearest-value search in double).  NVFP4 works
@@ -318,6 +321,59 @@ void or_nv_dequantize(const uint8_t *q, const uint8_t *s, float gscale,
             y[r * k + i] = (double)gscale *
                            or_e4m3_decode(s[r * nb + i / 16]) *
                            or_e2m1_decode(c);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Block Hadamard rotation ahead of quantization                       */
+/* ------------------------------------------------------------------ */
+
+/* An orthogonal H per block, y_j = H_j x_j, which keeps the 2-norm, so the
+ * quantization error can be judged in the rotated domain [TRANSFP4 sec. 2.3
+ * eq. (2)]; the activation side computes X H_k online with a butterfly
+ * network, k in {16, 32, 64, 128} [ANALYSIS sec. 3.2.3].
+ *
+ * H_hk here is the Sylvester-ordered Hadamard matrix divided by sqrt(hk)
+ * (orthonormal, symmetric): H[i][j] = (-1)^popcount(i & j) / sqrt(hk).  In
+ * fp32 the rotation is not exact, so its order of operations is part of the
+ * definition (the codes are decided on the rotated fp32 values): the fast
+ * transform over h = 1, 2, 4, ..., hk/2, every pair (i, i + h) with
+ * (i & h) == 0 replaced by (u + v, u - v), each sum rounded to fp32, then
+ * every element multiplied by the fp32 number nearest 1/sqrt(hk). */
+static float hadamard_norm_f32(int hk)
+{
+    return (float)(1.0 / sqrt((double)hk));
+}
+
+static void fwht_block_f32(float *v, int hk)
+{
+    for (int h = 1; h < hk; h *= 2)
+        for (int i = 0; i < hk; i++)
+            if ((i & h) == 0) {
+                float u = v[i], w = v[i + h];
+                v[i] = u + w;
+                v[i + h] = u - w;
+            }
+    const float c = hadamard_norm_f32(hk);
+    for (int i = 0; i < hk; i++)
+        v[i] = v[i] * c;
+}
+
+float or_hadamard_norm(int hk) { return hadamard_norm_f32(hk); }
+
+/* y[rows][k] (fp32) = x rotated block by block along k with H_hk; k must be
+ * a multiple of hk. */
+void or_hadamard_rotate(const void *x, int dtype, int64_t rows, int64_t k,
+                        int hk, float *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < k / hk; b++) {
+            float *v = y + r * k + b * hk;
+            for (int i = 0; i < hk; i++)
+                v[i] = load_elem(x, dtype, r * k + b * hk + i);
+            fwht_block_f32(v, hk);
         }
     }
 }

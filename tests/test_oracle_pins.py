@@ -389,6 +389,107 @@ def test_table5_order_of_magnitude_diagnostic():
         assert abs(c - 1 / math.sqrt(1 + nm)) < 2e-3
 
 
+# ------------------------------------------------------------------ block Hadamard rotation
+
+def _nearest_f32(exact):
+    """The fp32 nearest to a Fraction (ties to even), by comparing neighbours."""
+    from fractions import Fraction
+    c = np.float32(float(exact))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - exact)
+        if best is None or d < best[0] or (d == best[0] and (int(cand.view(np.uint32)) & 1) == 0):
+            best = (d, cand)
+    return best[1]
+
+
+def test_hadamard_norm_is_nearest_f32_of_inverse_sqrt():
+    """1/sqrt(hk): exact powers of two for 16 and 64; for 32 and 128 the fp32
+    nearest to 1/(4 sqrt 2) and 1/(8 sqrt 2), from a 60-digit square root."""
+    from decimal import Decimal, getcontext
+    from fractions import Fraction
+    getcontext().prec = 60
+    assert oracle.hadamard_norm(16) == 0.25 and oracle.hadamard_norm(64) == 0.125
+    for hk in (32, 128):
+        exact = Fraction(Decimal(1) / Decimal(hk).sqrt())
+        assert np.float32(oracle.hadamard_norm(hk)) == _nearest_f32(exact)
+
+
+@pytest.mark.parametrize("hk", [16, 32, 64, 128])
+def test_hadamard_matches_sylvester_matrix_on_exact_inputs(hk):
+    """Small integers: every butterfly sum is exact in fp32, so the rotated
+    block is fl32(c * (H x)) with H the Sylvester Hadamard matrix of the
+    library routine scipy.linalg.hadamard (entries (-1)^popcount(i & j))."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(hk)
+    x = rng.integers(-3, 4, size=(5, 2 * hk)).astype(np.float32)
+    H = hadamard(hk).astype(np.float64)
+    c = np.float32(oracle.hadamard_norm(hk))
+    y = oracle.hadamard_rotate(x, hk)
+    for b in range(2):
+        exact = x[:, b * hk:(b + 1) * hk].astype(np.float64) @ H.T
+        assert np.array_equal(y[:, b * hk:(b + 1) * hk], exact.astype(np.float32) * c)
+
+
+@pytest.mark.parametrize("hk", [16, 32, 64, 128])
+def test_hadamard_rotation_within_fp32_error_bound(hk):
+    """General inputs: each output is a +-sum of the block's hk inputs by a
+    tree of depth log2(hk), then one multiply, so |y - H x| <= (log2(hk) + 1)
+    u sum|x| / sqrt(hk) with u = 2^-24 (a wrong sign or index breaks this by
+    far); and H is orthonormal and symmetric: rotating twice returns x."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(7 + hk)
+    x = (rng.standard_normal((64, 4 * hk)) * np.exp2(rng.integers(-20, 21, size=(64, 1)))).astype(np.float32)
+    H = hadamard(hk).astype(np.float64) / math.sqrt(hk)
+    y = oracle.hadamard_rotate(x, hk).astype(np.float64)
+    xd = x.astype(np.float64)
+    for b in range(4):
+        sl = slice(b * hk, (b + 1) * hk)
+        exact = xd[:, sl] @ H.T
+        bound = (math.log2(hk) + 1) * 2.0 ** -24 * np.abs(xd[:, sl]).sum(axis=1, keepdims=True) / math.sqrt(hk)
+        assert np.all(np.abs(y[:, sl] - exact) <= bound)
+        back = oracle.hadamard_rotate(y[:, sl].astype(np.float32), hk).astype(np.float64)
+        assert np.allclose(back, xd[:, sl], rtol=0, atol=4 * (math.log2(hk) + 1) * 2.0 ** -24
+                           * np.abs(xd[:, sl]).sum(axis=1, keepdims=True).max())
+
+
+def test_hadamard_error_identity_eq2():
+    """||x - H^T Q(H x)|| = ||H x - Q(H x)|| for orthogonal H [TransFP4 page
+    sec. 2.3 eq. (2)], with Q = MXFP4 quantize-dequantize of the rotated
+    values (computed here in double from the oracle's fp32 rotation)."""
+    from scipy.linalg import hadamard
+    x = synth.table4_activations(n=32 * 512, seed=3).reshape(16, -1)
+    H = hadamard(32).astype(np.float64) / math.sqrt(32)
+    y = oracle.hadamard_rotate(x, 32)
+    q, s = oracle.mx_quantize(y)
+    yh = oracle.mx_dequantize(q, s)
+    xh = (yh.reshape(-1, 32) @ H).reshape(x.shape)  # H^T = H
+    lhs = np.linalg.norm(x.astype(np.float64) - xh)
+    rhs = np.linalg.norm(y.astype(np.float64) - yh)
+    assert abs(lhs - rhs) <= 1e-5 * rhs
+
+
+def test_rotated_mxfp4_table5_diagnostic():
+    """Loose check against Table 5's rotated-MXFP4 row (32-point Hadamard):
+    rotation lowers the MXFP4 error on the heavy-tailed activations, to the
+    printed order of magnitude.  Parity unpinned beyond that (seeds and the
+    page's exact rotation are not printed)."""
+    rows = {r[0]: (float(r[1]), float(r[2])) for r in golden_lines("table5_nmse.txt")}
+    from scipy.linalg import hadamard
+    x = synth.table4_activations()
+    xd = x.astype(np.float64).reshape(1, -1)
+    H = hadamard(32).astype(np.float64) / math.sqrt(32)
+    y = oracle.hadamard_rotate(x, 32)
+    q, s = oracle.mx_quantize(y)
+    xh = (oracle.mx_dequantize(q, s).reshape(-1, 32) @ H).reshape(xd.shape)
+    nm_rot, c_rot = oracle.metrics(xd, xh)
+    q0, s0 = oracle.mx_quantize(x)
+    nm_mx, _ = oracle.metrics(xd, oracle.mx_dequantize(q0, s0))
+    assert nm_rot < nm_mx
+    assert rows["ROTATED_MXFP4"][0] / 3 < nm_rot < rows["ROTATED_MXFP4"][0] * 3
+    assert abs(c_rot - 1 / math.sqrt(1 + nm_rot)) < 2e-3
+
+
 # ------------------------------------------------------------------ layout / bit widths
 
 def test_bit_widths_and_scale_counts():
