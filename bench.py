@@ -5,7 +5,8 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--only parts] [--no-cpu-bas
 One step runs every row of the hot path once, on seeded synthetic inputs
 already resident in HBM:
   tiny   MXFP4 quantize (fp32 256x512) + dequantize + W4A16 GEMV (m=1)
-  quant  dynamic MXFP4 quantize of bf16 activations 16384x8192
+  quant  dynamic MXFP4 quantize of bf16 activations 16384x8192, plain and
+         with the 32-point block Hadamard rotation fused ahead of it
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
   c5     NVFP4 and MXFP4 quantize of W 8192x4096 and X 4096x4096, and the
@@ -137,6 +138,9 @@ def main():
                  torch.empty((16384, 256), dtype=u8, device=dev)) for c in range(n3)]
         ops.append(("quantize_16384x8192_bf16", rotating(sets, lambda x, q, s: mxq.quantize(x, q, s)),
                     quant_bytes(16384, 8192), 0))
+        # rotated MXFP4 (32-point block Hadamard fused ahead of the quantizer)
+        ops.append(("quantize_hadamard32_16384x8192_bf16",
+                    rotating(sets, lambda x, q, s: mxq.quantize_hadamard(x, 32, q, s)), quant_bytes(16384, 8192), 0))
     if "gemv" in parts:
         n2, k2 = 28672, 8192
         w2, _ = synth.decode_gemv(1)

@@ -102,6 +102,26 @@ MXQ_API mxq_status mxq_quantize(const void *x, mxq_dtype xdt, int64_t rows, int6
                         uint8_t *q, uint8_t *s, hipStream_t stream);
 
 /*
+ * Rotated MXFP4 quantize: the MXFP4 codes and scales (as mxq_quantize) of
+ * y = x rotated block by block along k with H_hk, the Sylvester-ordered
+ * Hadamard matrix divided by sqrt(hk) (orthonormal and symmetric, so the
+ * rotation is undone by applying it again, and Y = X W^T equals the product
+ * of the rotated X and W).  hk is 16, 32, 64 or 128; k % 32 == 0 and
+ * k % hk == 0.  The rotation is computed in fp32 in a fixed order: butterfly
+ * stages h = 1, 2, ..., hk/2, each pair (i, i + h) -> (u + v, u - v), then
+ * a multiply by the fp32 nearest 1/sqrt(hk); the codes are decided on those
+ * fp32 values.  x[rows][k] (xdt), q[rows][k/2], s[rows][k/32].
+ * [TransFP4 page sec. 2.3 eq. (2): an orthogonal H_j per block keeps the
+ * 2-norm; "FP4 quantization analysis" page sec. 3.2.3: block-diagonal
+ * Hadamard H_k, k in {16, 32, 64, 128}, computed online for activations.]
+ * Errors: INVALID_VALUE for any other hk or a k not a multiple of 32 and
+ * hk, as well as the cases of mxq_quantize.
+ */
+MXQ_API mxq_status mxq_quantize_hadamard(const void *x, mxq_dtype xdt, int64_t rows,
+                                 int64_t k, int hk, uint8_t *q, uint8_t *s,
+                                 hipStream_t stream);
+
+/*
  * MXFP4 dequantize.  (q[rows][k/2], s[rows][k/32]) -> y[rows][k] of type ydt:
  * y = E2M1(code) * 2^(s - 127), exact in fp32 and bf16 for scale codes
  * 1..250 [TransFP4 page eq. (1) with s_g = 1].  Scale code 255 (NaN in E8M0)

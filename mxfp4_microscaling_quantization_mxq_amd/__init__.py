@@ -32,8 +32,8 @@ STATUS = {
     4: "MXQ_ERROR_LAUNCH_FAILURE",
 }
 API = (
-    "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_dequantize", "mxq_gemv_w4a16",
-    "mxq_gemm_w4a4", "nvq_quantize", "nvq_dequantize", "nvq_gemm",
+    "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_dequantize",
+    "mxq_gemv_w4a16", "mxq_gemm_w4a4", "nvq_quantize", "nvq_dequantize", "nvq_gemm",
 )
 
 
@@ -63,6 +63,7 @@ def capi() -> ctypes.CDLL:
     lib.mxq_version.argtypes = []
     lib.mxq_version.restype = I
     lib.mxq_quantize.argtypes = [P, I, I64, I64, P, P, P]
+    lib.mxq_quantize_hadamard.argtypes = [P, I, I64, I64, I, P, P, P]
     lib.mxq_dequantize.argtypes = [P, P, I64, I64, P, I, P]
     lib.mxq_gemv_w4a16.argtypes = [P, P, I64, I64, P, I64, P, I, P]
     lib.mxq_gemm_w4a4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
@@ -133,6 +134,21 @@ def quantize(x, q=None, s=None):
     if s is None:
         s = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
     _check(capi().mxq_quantize(_p(x), _dtype_code(x.dtype), rows, k, _p(q), _p(s), _stream()), "mxq_quantize")
+    return q, s
+
+
+def quantize_hadamard(x, hk=32, q=None, s=None):
+    """Rotated MXFP4: quantize x[rows, k] after the orthonormal block Hadamard
+    H_hk along k (hk in 16, 32, 64, 128) -> (q[rows, k/2] u8, s[rows, k/32] u8)."""
+    torch = _torch()
+    _need(x, "x")
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _check(capi().mxq_quantize_hadamard(_p(x), _dtype_code(x.dtype), rows, k, int(hk), _p(q), _p(s), _stream()),
+           "mxq_quantize_hadamard")
     return q, s
 
 

@@ -80,6 +80,19 @@ mxq_status mxq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, u
   return launched(mxq::launch_mx_quantize(x, xdt == MXQ_BF16, rows, k, q, s, stream));
 }
 
+mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, int hk, uint8_t* q,
+                                 uint8_t* s, hipStream_t stream) {
+  if (hk != 16 && hk != 32 && hk != 64 && hk != 128) return MXQ_ERROR_INVALID_VALUE;
+  if (rows < 0 || k < 0 || k % 32 != 0 || k % hk != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
+  if (!x || !q || !s) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_mx_quantize_hadamard(x, xdt == MXQ_BF16, rows, k, hk, q, s, stream));
+}
+
 mxq_status mxq_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y, mxq_dtype ydt,
                           hipStream_t stream) {
   if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;

@@ -10,6 +10,10 @@ namespace mxq {
 
 hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
                               hipStream_t st);
+// MXFP4 of x rotated block by block along k with the orthonormal Hadamard
+// H_hk, hk in {16, 32, 64, 128}, k % max(32, hk) == 0.
+hipError_t launch_mx_quantize_hadamard(const void* x, bool bf16, int64_t rows, int64_t k, int hk, uint8_t* q,
+                                       uint8_t* s, hipStream_t st);
 hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y,
                                 bool bf16, hipStream_t st);
 hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,

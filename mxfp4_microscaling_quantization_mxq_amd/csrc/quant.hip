@@ -98,6 +98,112 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restric
   }
 }
 
+// ---------------------------------------------------------------- rotated MXFP4
+
+// Block Hadamard rotation fused ahead of the MXFP4 quantizer: y_j = H x_j
+// per block of HK elements along k, H the Sylvester-ordered Hadamard matrix
+// divided by sqrt(HK) (orthonormal, so the error can be judged in the
+// rotated domain [TransFP4 page sec. 2.3 eq. (2)]; the activation side
+// computes X H_k online with a butterfly network, k in {16, 32, 64, 128}
+// ["FP4 quantization analysis" page, sec. 3.2.3]).  In fp32 the rotation
+// rounds, so its order of operations is fixed: butterfly stages h = 1, 2,
+// 4, ..., HK/2 over pairs (i, i + h), (u, v) -> (u + v, u - v), then one
+// multiply by the fp32 nearest 1/sqrt(HK).  A lane holds 8 consecutive
+// elements: stages h < 8 run inside the lane, h = 8 m between lanes l and
+// l ^ m (the lane with bit m clear keeps the sum, the other partner - own =
+// u - v).  The rotated fp32 values then go through the fp32 MXFP4 path.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1)
+    return __uint_as_float(dpp_quad_xor1(__float_as_uint(v)));
+  else if constexpr (M == 2)
+    return __uint_as_float(dpp_quad_xor2(__float_as_uint(v)));
+  else if constexpr (M == 4)
+    return __shfl_xor(v, 4, 64);
+  else  // row_ror:8 inside a row of 16 lanes: lane l ^ 8
+    return __uint_as_float((unsigned)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x128, 0xF, 0xF, false));
+}
+
+template <int HK>
+__device__ __forceinline__ float hadamard_norm() {
+  // 1/sqrt(16) and 1/sqrt(64) are exact; for 32 and 128 the fp32 nearest
+  // 1/sqrt(2) (0x3F3504F3) divided exactly by 4 and by 8
+  if constexpr (HK == 16) return 0.25f;
+  else if constexpr (HK == 32) return 0x1.6a09e6p-3f;
+  else if constexpr (HK == 64) return 0.125f;
+  else return 0x1.6a09e6p-4f;
+}
+
+template <int M>
+__device__ __forceinline__ void butterfly_across_lanes(float (&v)[8], int lane) {
+  const bool upper = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float p = lane_xor<M>(v[i]);
+    v[i] = upper ? p - v[i] : v[i] + p;
+  }
+}
+
+template <bool kBf16In, int HK>
+__global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __restrict__ x, unsigned* __restrict__ q,
+                                                              uint8_t* __restrict__ s, int64_t nlanes) {
+  static_assert(HK == 16 || HK == 32 || HK == 64 || HK == 128, "rotation size");
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // nlanes is a multiple of HK / 8 and of 4, and blocks hold 256 lanes:
+  // rotation groups and MXFP4 quads are whole or absent
+  if (t >= nlanes) return;
+  const int lane = threadIdx.x & 63;
+  float v[8];
+  if (kBf16In) {
+    const u32x4 w = __builtin_nontemporal_load(&x[t]);
+    const unsigned ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(ww[i] << 16);
+      v[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+    }
+  } else {
+    const u32x4 a = __builtin_nontemporal_load(&x[2 * t]);
+    const u32x4 b = __builtin_nontemporal_load(&x[2 * t + 1]);
+    const unsigned ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = __uint_as_float(ww[i]);
+  }
+  // stages h = 1, 2, 4 inside the lane
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if ((i & h) == 0) {
+        const float u = v[i], w = v[i + h];
+        v[i] = u + w;
+        v[i + h] = u - w;
+      }
+  // stages h = 8, 16, 32, 64 across lanes 1, 2, 4, 8 apart
+  if constexpr (HK > 8) butterfly_across_lanes<1>(v, lane);
+  if constexpr (HK > 16) butterfly_across_lanes<2>(v, lane);
+  if constexpr (HK > 32) butterfly_across_lanes<4>(v, lane);
+  if constexpr (HK > 64) butterfly_across_lanes<8>(v, lane);
+  const float c = hadamard_norm<HK>();
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = v[i] * c;
+  // MXFP4 of the rotated block (as k_mx_quantize_f32)
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  const unsigned code = e8m0_code_from_expfield(m >> 23);
+  const float scale = e8m0_as_scale(code);
+  unsigned out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], scale, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], scale, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], scale, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], scale, 3);
+  q[t] = out;
+  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+}
+
 // ---------------------------------------------------------------- NVFP4
 
 // Tensor amax [infra-guide sec. 2: s = max|x| / F_max], in two steps with
@@ -287,6 +393,30 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
   else
     hipLaunchKernelGGL(k_mx_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
                        (unsigned*)q, s, nlanes);
+  return hipGetLastError();
+}
+
+template <int HK>
+static void launch_mx_quantize_hadamard_hk(const void* x, bool bf16, int64_t nlanes, uint8_t* q, uint8_t* s,
+                                           hipStream_t st) {
+  if (bf16)
+    hipLaunchKernelGGL((k_mx_quantize_hadamard<true, HK>), dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const u32x4*)x, (unsigned*)q, s, nlanes);
+  else
+    hipLaunchKernelGGL((k_mx_quantize_hadamard<false, HK>), dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+                       (const u32x4*)x, (unsigned*)q, s, nlanes);
+}
+
+hipError_t launch_mx_quantize_hadamard(const void* x, bool bf16, int64_t rows, int64_t k, int hk, uint8_t* q,
+                                       uint8_t* s, hipStream_t st) {
+  const int64_t nlanes = rows * k / 8;
+  switch (hk) {
+    case 16: launch_mx_quantize_hadamard_hk<16>(x, bf16, nlanes, q, s, st); break;
+    case 32: launch_mx_quantize_hadamard_hk<32>(x, bf16, nlanes, q, s, st); break;
+    case 64: launch_mx_quantize_hadamard_hk<64>(x, bf16, nlanes, q, s, st); break;
+    case 128: launch_mx_quantize_hadamard_hk<128>(x, bf16, nlanes, q, s, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -69,6 +69,18 @@ def test_quantize_validation(lib):
     assert q(NULL, 1, 4, 0, NULL, NULL, NULL) == SUCCESS
 
 
+def test_quantize_hadamard_validation(lib):
+    q = lib.mxq_quantize_hadamard
+    for hk in (0, 8, 24, 256, -32):
+        assert q(A16, 1, 4, 128, hk, A16b, A16c, NULL) == INVALID  # rotation size
+    assert q(A16, 1, 4, 96, 64, A16b, A16c, NULL) == INVALID  # k % hk
+    assert q(A16, 1, 4, 48, 16, A16b, A16c, NULL) == INVALID  # k % 32
+    assert q(A16, 7, 4, 64, 32, A16b, A16c, NULL) == INVALID  # bad dtype
+    assert q(NULL, 1, 4, 64, 32, A16b, A16c, NULL) == INVALID
+    assert q(A16, 1, 4, 64, 32, A16b, MIS, NULL) == MISALIGNED
+    assert q(NULL, 1, 0, 64, 32, NULL, NULL, NULL) == SUCCESS  # empty
+
+
 def test_dequantize_validation(lib):
     d = lib.mxq_dequantize
     assert d(A16, A16b, 4, 40, A16c, 1, NULL) == INVALID
@@ -120,6 +132,7 @@ def test_no_device_reports_not_supported(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: this case is only safe without one")
     assert lib.mxq_quantize(A16, 1, 4, 32, A16b, A16c, NULL) == NOT_SUPPORTED
+    assert lib.mxq_quantize_hadamard(A16, 1, 4, 32, 32, A16b, A16c, NULL) == NOT_SUPPORTED
     assert lib.mxq_gemm_w4a4(A16, A16b, A16c, A16d, 4, 4, 32, A16, 1, NULL) == NOT_SUPPORTED
     assert lib.nvq_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, NULL) == NOT_SUPPORTED
 

@@ -165,6 +165,62 @@ def test_mx_dequantize_every_byte_and_scale():
         assert same.all(), f"{nm}: {np.argwhere(~same)[:5].tolist()}"
 
 
+# ------------------------------------------------------------------ rotated MXFP4
+
+@pytest.mark.parametrize("hk", [16, 32, 64, 128])
+@pytest.mark.parametrize("rows,k", [(1, 128), (37, 384), (300, 2048)])
+def test_mx_quantize_hadamard_ragged(hk, rows, k):
+    """Codes and scales bit-exact against the oracle's fp32 rotation +
+    MXFP4, for bf16 and fp32 inputs with per-row magnitude spreads."""
+    for x_np, nm in [(laplace_bf16(rows * 7 + k + hk, rows, k), "bf16"), (laplace_f32(rows + 3 * k + hk, rows, k), "fp32")]:
+        q, s = mxq.quantize_hadamard(dev(x_np), hk)
+        qo, so = oracle.mx_quantize_hadamard(x_np, hk)
+        assert np.array_equal(host(s), so), f"hk={hk} {nm} {rows}x{k}: scale mismatch"
+        assert np.array_equal(host(q), qo), f"hk={hk} {nm} {rows}x{k}: code mismatch"
+
+
+def test_mx_quantize_hadamard_edge_values():
+    """Zeros, signed zeros, a lone outlier per block, huge and tiny values."""
+    x = np.zeros((8, 256), dtype=np.float32)
+    x[1, :] = -0.0
+    x[2, 5] = 1e30
+    x[3, ::7] = -3.5e-30
+    x[4, :] = np.exp2(np.linspace(-40, 40, 256)).astype(np.float32)
+    x[5, 100] = -7.0
+    x[6, :128] = 1e36  # block sums stay inside the fp32 range
+    x[7, :] = np.linspace(-6, 6, 256, dtype=np.float32)
+    for hk in (16, 32, 64, 128):
+        q, s = mxq.quantize_hadamard(dev(x), hk)
+        qo, so = oracle.mx_quantize_hadamard(x, hk)
+        assert np.array_equal(host(s), so) and np.array_equal(host(q), qo), f"hk={hk}"
+
+
+def test_mx_quantize_hadamard_dynamic_full_size():
+    """The 16384 x 8192 activation tensor through the 32-point rotation."""
+    x = dynamic_quantize_input()
+    q, s = mxq.quantize_hadamard(dev(x), 32)
+    qo, so = oracle.mx_quantize_hadamard(x, 32)
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+
+
+def test_rotated_operands_keep_the_product():
+    """H is orthonormal, so (X H)(W H)^T = X W^T: the W4A4 GEMM of rotated
+    MXFP4 operands approximates the unquantized product (and more closely than
+    unrotated MXFP4 on these heavy-tailed inputs)."""
+    w, x = synth.nv_vs_mx(n=256, m=128, k=1024)
+    ref, _ = oracle.gemm_nt(synth.bf16_bits_to_f32(x).astype(np.float64), synth.bf16_bits_to_f32(w).astype(np.float64))
+    qx, sx = mxq.quantize_hadamard(dev(x), 32)
+    qw, sw = mxq.quantize_hadamard(dev(w), 32)
+    c_rot = host(mxq.gemm_w4a4(qx, sx, qw, sw, torch.float32)).astype(np.float64)
+    qx0, sx0 = mxq.quantize(dev(x))
+    qw0, sw0 = mxq.quantize(dev(w))
+    c0 = host(mxq.gemm_w4a4(qx0, sx0, qw0, sw0, torch.float32)).astype(np.float64)
+    nm_rot, _ = oracle.metrics(ref, c_rot)
+    nm0, _ = oracle.metrics(ref, c0)
+    say(f"W4A4 product NMSE: rotated MXFP4 {nm_rot:.5f}, MXFP4 {nm0:.5f}")
+    assert nm_rot < nm0 and nm_rot < 0.05
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def assert_nv(x_np, gscale, what):
