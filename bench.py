@@ -9,6 +9,7 @@ already resident in HBM:
          with the 32-point block Hadamard rotation fused ahead of it
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
+         (bf16 output, and MXFP4 output quantized in the epilogue)
   c5     NVFP4 and MXFP4 quantize of W 8192x4096 and X 4096x4096, and the
          W4A16 GEMM Y = X W^T (4096x8192x4096) in each format
 Every HBM-bound op cycles through copies of its operands whose combined size
@@ -171,6 +172,12 @@ def main():
         # the GEMM is compute-bound (its 68 MB of operands may stay in the cache)
         ops.append(("gemm_w4a4_8192", lambda: mxq.gemm_w4a4(qa4, sa4, qb4, sb4, c=c4),
                     2 * mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3))
+        # the same product with the MXFP4 quantization of its output fused
+        # into the epilogue (the next layer's activations, no bf16 round trip)
+        cq4 = torch.empty((8192, 4096), dtype=u8, device=dev)
+        cs4 = torch.empty((8192, 256), dtype=u8, device=dev)
+        ops.append(("gemm_w4a4_8192_mxfp4_out", lambda: mxq.gemm_w4a4_quant(qa4, sa4, qb4, sb4, cq4, cs4),
+                    3 * mx_bytes(8192, 8192), 2 * 8192 ** 3))
     if "c5" in parts:
         w5, x5 = synth.nv_vs_mx()
         w5d, x5d = to_dev(w5), to_dev(x5)
@@ -284,7 +291,7 @@ def main():
 
     rooflines = {}
     for name in per_op:
-        if name.startswith("gemm_w4a4"):
+        if name.startswith("gemm_w4a4"):  # both output kinds
             rooflines[name] = roof(name, "mfma_fp4")
         elif "gemm_w4a16_4096" in name:
             rooflines[name] = roof(name, "mfma_bf16")

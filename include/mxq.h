@@ -158,6 +158,22 @@ MXQ_API mxq_status mxq_gemm_w4a4(const uint8_t *aq, const uint8_t *as,
                          hipStream_t stream);
 
 /*
+ * W4A4 product with MXFP4 output: c = bf16(A_hat B_hat^T) computed as in
+ * mxq_gemm_w4a4 with bf16 output, then quantized to MXFP4 along n in the
+ * kernel's epilogue, so the 16-bit product never reaches memory.  The codes
+ * cq[m][n/2] and E8M0 scales cs[m][n/32] are bit-identical to mxq_quantize
+ * of the bf16 product (the same quantizer runs on the same bf16 values).
+ * n % 32 == 0, k % 32 == 0; k == 0 writes the codes of a zero product.
+ * [TransFP4 page sec. 2.5: no 16-bit copy is materialized; "FP4
+ * quantization analysis" page, QuTLASS kernel section: custom epilogues
+ * fuse the quantization of the output.]
+ */
+MXQ_API mxq_status mxq_gemm_w4a4_quant(const uint8_t *aq, const uint8_t *as,
+                               const uint8_t *bq, const uint8_t *bs, int64_t m,
+                               int64_t n, int64_t k, uint8_t *cq, uint8_t *cs,
+                               hipStream_t stream);
+
+/*
  * NVFP4 quantize.  x[rows][k] (xdt) -> q[rows][k/2] packed E2M1 codes,
  * s[rows][k/16] E4M3 block-scale codes, and the fp32 tensor scale *gscale
  * (a single float in device memory, the dequantization multiplier).

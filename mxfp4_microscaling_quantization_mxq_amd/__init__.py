@@ -33,7 +33,7 @@ STATUS = {
 }
 API = (
     "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_dequantize",
-    "mxq_gemv_w4a16", "mxq_gemm_w4a4", "nvq_quantize", "nvq_dequantize", "nvq_gemm",
+    "mxq_gemv_w4a16", "mxq_gemm_w4a4", "mxq_gemm_w4a4_quant", "nvq_quantize", "nvq_dequantize", "nvq_gemm",
 )
 
 
@@ -67,6 +67,7 @@ def capi() -> ctypes.CDLL:
     lib.mxq_dequantize.argtypes = [P, P, I64, I64, P, I, P]
     lib.mxq_gemv_w4a16.argtypes = [P, P, I64, I64, P, I64, P, I, P]
     lib.mxq_gemm_w4a4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    lib.mxq_gemm_w4a4_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
     lib.nvq_quantize.argtypes = [P, I, I64, I64, P, I, P, P, P]
     lib.nvq_dequantize.argtypes = [P, P, P, I64, I64, P, I, P]
     lib.nvq_gemm.argtypes = [P, P, P, I64, I64, P, I64, P, I, P]
@@ -198,6 +199,25 @@ def gemm_w4a4(aq, as_, bq, bs, out_dtype=None, c=None):
     _check(capi().mxq_gemm_w4a4(_p(aq), _p(as_), _p(bq), _p(bs), m, n, k, _p(c), _dtype_code(c.dtype), _stream()),
            "mxq_gemm_w4a4")
     return c
+
+
+def gemm_w4a4_quant(aq, as_, bq, bs, cq=None, cs=None):
+    """W4A4 with MXFP4 output: (cq[m, n/2], cs[m, n/32]) = MXFP4 of the
+    bf16-rounded deq(A) @ deq(B)^T, quantized in the GEMM epilogue."""
+    torch = _torch()
+    for t, nm in ((aq, "aq"), (as_, "as"), (bq, "bq"), (bs, "bs")):
+        _need(t, nm, torch.uint8)
+    m, k = aq.shape[0], aq.shape[1] * 2
+    n = bq.shape[0]
+    if bq.shape[1] * 2 != k:
+        raise ValueError("A and B disagree on k")
+    if cq is None:
+        cq = torch.empty((m, n // 2), dtype=torch.uint8, device=aq.device)
+    if cs is None:
+        cs = torch.empty((m, n // 32), dtype=torch.uint8, device=aq.device)
+    _check(capi().mxq_gemm_w4a4_quant(_p(aq), _p(as_), _p(bq), _p(bs), m, n, k, _p(cq), _p(cs), _stream()),
+           "mxq_gemm_w4a4_quant")
+    return cq, cs
 
 
 # ------------------------------------------------------------------ NVFP4

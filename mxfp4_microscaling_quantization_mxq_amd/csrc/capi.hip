@@ -155,6 +155,28 @@ mxq_status mxq_gemm_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq
   return launched(mxq::launch_w4a4(aq, as, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
 }
 
+mxq_status mxq_gemm_w4a4_quant(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                               int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || n % 32 != 0) return MXQ_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return MXQ_SUCCESS;
+  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (!cq || !cs) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(cq) || !aligned16(cs)) return MXQ_ERROR_MISALIGNED;
+  if (k == 0) {
+    // the product is zero: the codes and scales of quantizing zeros
+    mxq_status d = check_device();
+    if (d != MXQ_SUCCESS) return d;
+    mxq_status e = launched(mxq::launch_zero_bytes(cq, m * n / 2, stream));
+    if (e != MXQ_SUCCESS) return e;
+    return launched(mxq::launch_zero_bytes(cs, m * n / 32, stream));
+  }
+  if (!aq || !as || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_w4a4_mx(aq, as, bq, bs, m, n, k, cq, cs, stream));
+}
+
 mxq_status nvq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, float* gscale, int compute_gscale,
                         uint8_t* q, uint8_t* s, hipStream_t stream) {
   if (rows < 0 || k < 0 || k % 16 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;

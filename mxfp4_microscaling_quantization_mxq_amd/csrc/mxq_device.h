@@ -109,4 +109,30 @@ __device__ __forceinline__ unsigned short bf16_rne_of_sum(float p, float err) {
   return f32_to_bf16_rne(p);
 }
 
+// MXFP4 of one lane's 8 consecutive bf16 values, four lanes (a DPP quad,
+// all of it active) forming one 32-element block: block absmax as an integer
+// max of magnitude bits shared over the quad, E8M0 code = max(expfield - 2,
+// 0), then the scaled convert (round to nearest even, saturation at 6,
+// signed zeros).  Returns the 8 codes packed, element 2j in the low nibble
+// of byte j, and sets *code to the block's E8M0 code.  Every MXFP4
+// quantizer of bf16 data in the library goes through this function.
+__device__ __forceinline__ unsigned mx_quantize_quad_bf16(bf16x8 xb, unsigned* code) {
+  // The convert's bf16 pairs are built from bf16x8 elements: feeding it a
+  // bit_cast<bf16x2>(uint) miscompiled (every call got the first dword).
+  const u32x4 v = __builtin_bit_cast(u32x4, xb);
+  unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
+  m = max(m & 0xFFFFu, m >> 16);
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  const unsigned c = e8m0_code_from_expfield(m >> 7);
+  const float scale = e8m0_as_scale(c);
+  unsigned out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[0], xb[1]}, scale, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[2], xb[3]}, scale, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[4], xb[5]}, scale, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[6], xb[7]}, scale, 3);
+  *code = c;
+  return out;
+}
+
 }  // namespace mxq

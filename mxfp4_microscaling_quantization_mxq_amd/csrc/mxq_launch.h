@@ -30,6 +30,14 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
 hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
 
+// W4A4 with the product rounded to bf16 and quantized to MXFP4 along n in
+// the epilogue: cq[m][n/2], cs[m][n/32]; n % 32 == 0.
+hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                          int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t st);
+
+// Fills n bytes of y with zeros.
+hipError_t launch_zero_bytes(uint8_t* y, int64_t n, hipStream_t st);
+
 // Fills n elements of y (fp32 or bf16) with zeros.
 hipError_t launch_zero(void* y, int64_t n, bool bf16, hipStream_t st);
 

@@ -28,22 +28,9 @@ __global__ __launch_bounds__(256) void k_mx_quantize_bf16(const u32x4* __restric
                                                           int64_t nlanes) {
   int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nlanes) return;  // nlanes is a multiple of 4: quads stay whole
-  // The convert's bf16 pairs are built from bf16x8 elements: feeding it a
-  // bit_cast<bf16x2>(uint) miscompiles (every call got the first dword).
-  bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
-  u32x4 v = __builtin_bit_cast(u32x4, xb);
-  unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
-  m = max(m & 0xFFFFu, m >> 16);
-  m = max(m, dpp_quad_xor1(m));
-  m = max(m, dpp_quad_xor2(m));
-  unsigned code = e8m0_code_from_expfield(m >> 7);
-  float scale = e8m0_as_scale(code);
-  unsigned out = 0;
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[0], xb[1]}, scale, 0);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[2], xb[3]}, scale, 1);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[4], xb[5]}, scale, 2);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[6], xb[7]}, scale, 3);
-  q[t] = out;
+  const bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
+  unsigned code;
+  q[t] = mx_quantize_quad_bf16(xb, &code);
   if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
 }
 

@@ -19,15 +19,46 @@
 
 namespace mxq {
 
+// Output kinds of the W4A4 kernels: fp32, bf16, or MXFP4 (the bf16-rounded
+// product quantized along n, bit-identical to mxq_quantize of the bf16
+// output: the quantizer is the same device function).
+constexpr int kOutF32 = 0, kOutBf16 = 1, kOutMx = 2;
+
+// Quantizes a bf16 output tile staged in LDS and stores its codes and E8M0
+// scales.  The tile has ROWS rows of COLS bytes (COLS / 16 units of 8 bf16);
+// rows [0, 128) sit in lo and [128, ROWS) in hi (two LDS variables when the
+// tile exceeds one), row r at (r % 128) * COLS bytes of its region, unit u
+// of row r at u ^ (r % (COLS / 16)).
+// Four consecutive threads take the four units (32 columns) of one MXFP4
+// block; blocks past m or n are computed but not stored (n % 32 == 0).
+template <int ROWS, int COLS>
+__device__ __forceinline__ void store_mx_tile(const uint8_t* lo, const uint8_t* hi, int64_t m0, int64_t n0,
+                                              int64_t m, int64_t n, uint8_t* __restrict__ cq,
+                                              uint8_t* __restrict__ cs) {
+  constexpr int UNITS = COLS / 16;  // 16-byte units (8 bf16) per row
+  for (int u = threadIdx.x; u < ROWS * UNITS; u += blockDim.x) {
+    const int r = u / UNITS, unit = u % UNITS;
+    const uint8_t* base = r < 128 ? lo : hi;
+    const bf16x8 xb = *(const bf16x8*)(base + (r & 127) * COLS + ((unit ^ (r % UNITS)) << 4));
+    unsigned code;
+    const unsigned codes = mx_quantize_quad_bf16(xb, &code);
+    const int64_t gr = m0 + r, gc = n0 + 8 * unit;
+    if (gr < m && gc < n) {
+      *(unsigned*)(cq + gr * (n / 2) + gc / 2) = codes;
+      if ((unit & 3) == 0) cs[gr * (n / 32) + gc / 32] = (uint8_t)code;
+    }
+  }
+}
+
 // First version: every wave streams its own operand fragments from global
 // memory (L2-resident) -- block tile 128 x 128, wave tile 64 x 64 = 2 x 2
 // MFMAs per 64-wide k step.
-template <bool kBf16Out>
+template <int OUT>
 __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__ aq,
                                                      const uint8_t* __restrict__ as,
                                                      const uint8_t* __restrict__ bq,
                                                      const uint8_t* __restrict__ bs, int64_t m, int64_t n,
-                                                     int64_t k, void* __restrict__ c) {
+                                                     int64_t k, void* __restrict__ c, uint8_t* __restrict__ cs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t row0 = (int64_t)blockIdx.y * 128 + 64 * wm;
@@ -75,6 +106,25 @@ __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__
                                                                       sb[j]);
   }
 
+  if constexpr (OUT == kOutMx) {
+    // bf16 tile staged in LDS, then quantized row-wise (16-byte unit u of
+    // tile row r at u ^ (r & 15))
+    __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 256];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int tr = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int tc = 64 * wn + 32 * j + r32;
+          *(uint16_t*)(tile + tr * 256 + (((tc >> 3) ^ (tr & 15)) << 4) + 2 * (tc & 7)) =
+              f32_to_bf16_rne(acc[i][j][r]);
+        }
+    __syncthreads();
+    store_mx_tile<128, 256>(tile, tile, (int64_t)blockIdx.y * 128, (int64_t)blockIdx.x * 128, m, n, (uint8_t*)c, cs);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -85,7 +135,7 @@ __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__
       for (int r = 0; r < 16; r++) {
         const int64_t rr = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
         if (rr >= m) continue;
-        if (kBf16Out)
+        if (OUT == kOutBf16)
           ((uint16_t*)c)[rr * n + cc] = f32_to_bf16_rne(acc[i][j][r]);
         else
           ((float*)c)[rr * n + cc] = acc[i][j][r];
@@ -167,12 +217,13 @@ __device__ __forceinline__ uint8_t* w4_scales() {
 // NWV waves per block: 4 (a 2 x 2 grid of 128 x 128 wave tiles, one wave
 // per SIMD) or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's
 // MFMAs cover the other's waits).
-template <int NWV, bool kBf16Out>
+template <int NWV, int OUT>
 __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
                                                            const uint8_t* __restrict__ bq,
                                                            const uint8_t* __restrict__ bs, int64_t m, int64_t n,
-                                                           int64_t k, void* __restrict__ c) {
+                                                           int64_t k, void* __restrict__ c,
+                                                           uint8_t* __restrict__ cs) {
   static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
   constexpr int WNC = NWV / 2;        // wave columns
   constexpr int WCOLS = kBN / WNC;    // output columns per wave
@@ -372,6 +423,33 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   }
   wait_vmcnt<0>();  // no copy may still target LDS when the block ends
 
+  if constexpr (OUT == kOutMx) {
+    // the bf16 tile into the two code slots (idle now that every wave has
+    // read its last fragments): rows 0..127 in slot 0, 128..255 in slot 1,
+    // 512 bytes per row, 16-byte unit u of row r at u ^ (r & 31)
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __syncthreads();
+    uint8_t* lo = w4_codes<0>();
+    uint8_t* hi = w4_codes<1>();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int tr = wm * 128 + i * 32 + r32;
+      uint8_t* rowp = (tr < 128 ? lo : hi) + (tr & 127) * 512;
+#pragma unroll
+      for (int j = 0; j < JB; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int tc = wn * WCOLS + j * 32 + q * 8 + 4 * half;
+          const u32x2 o = {f32_to_bf16_rne(acc[i][j][4 * q]) | ((unsigned)f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16),
+                           f32_to_bf16_rne(acc[i][j][4 * q + 2]) | ((unsigned)f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16)};
+          *(u32x2*)(rowp + (((tc >> 3) ^ (tr & 31)) << 4) + 2 * (tc & 7)) = o;
+        }
+    }
+    __syncthreads();
+    store_mx_tile<256, 512>(lo, hi, m0, n0, m, n, (uint8_t*)c, cs);
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t row = m0 + wm * 128 + i * 32 + r32;
@@ -384,7 +462,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
                     v3 = acc[i][j][4 * q + 3];
         if (col + 3 < n) {
-          if (kBf16Out) {
+          if (OUT == kOutBf16) {
             u32x2 o = {f32_to_bf16_rne(v0) | ((unsigned)f32_to_bf16_rne(v1) << 16),
                        f32_to_bf16_rne(v2) | ((unsigned)f32_to_bf16_rne(v3) << 16)};
             *(u32x2*)((uint16_t*)c + row * n + col) = o;
@@ -394,7 +472,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
         } else {
           const float vv[4] = {v0, v1, v2, v3};
           for (int e = 0; e < 4 && col + e < n; e++) {
-            if (kBf16Out)
+            if (OUT == kOutBf16)
               ((uint16_t*)c)[row * n + col + e] = f32_to_bf16_rne(vv[e]);
             else
               ((float*)c)[row * n + col + e] = vv[e];
@@ -410,23 +488,31 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
 #endif
 constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
 
-hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
-                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
+template <int OUT>
+static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                            int64_t n, int64_t k, void* c, uint8_t* cs, hipStream_t st) {
   if (k % 1024 == 0 && k >= 1024) {
     const unsigned tiles = (unsigned)(((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    if (bf16_out)
-      hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, true>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs, m,
-                         n, k, c);
-    else
-      hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, false>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs,
-                         m, n, k, c);
-    return hipGetLastError();
+    hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, OUT>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs, m,
+                       n, k, c, cs);
+    return;
   }
   dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
+  hipLaunchKernelGGL(k_w4a4_direct<OUT>, grid, dim3(256), 0, st, aq, as, bq, bs, m, n, k, c, cs);
+}
+
+hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
   if (bf16_out)
-    hipLaunchKernelGGL(k_w4a4_direct<true>, grid, dim3(256), 0, st, aq, as, bq, bs, m, n, k, c);
+    launch_w4a4_out<kOutBf16>(aq, as, bq, bs, m, n, k, c, nullptr, st);
   else
-    hipLaunchKernelGGL(k_w4a4_direct<false>, grid, dim3(256), 0, st, aq, as, bq, bs, m, n, k, c);
+    launch_w4a4_out<kOutF32>(aq, as, bq, bs, m, n, k, c, nullptr, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                          int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t st) {
+  launch_w4a4_out<kOutMx>(aq, as, bq, bs, m, n, k, cq, cs, st);
   return hipGetLastError();
 }
 
@@ -438,6 +524,16 @@ __global__ void k_zero(uint32_t* y, int64_t nwords) {
 __global__ void k_zero16(uint16_t* y, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = 0u;
+}
+
+__global__ void k_zero_bytes(uint8_t* y, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = 0u;
+}
+
+hipError_t launch_zero_bytes(uint8_t* y, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(void* y, int64_t n, bool bf16, hipStream_t st) {

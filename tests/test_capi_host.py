@@ -114,6 +114,16 @@ def test_w4a4_validation(lib):
     assert g(NULL, NULL, NULL, NULL, 0, 4, 32, NULL, 1, NULL) == SUCCESS
 
 
+def test_w4a4_quant_validation(lib):
+    g = lib.mxq_gemm_w4a4_quant
+    assert g(A16, A16b, A16c, A16d, 4, 48, 64, A16, A16b, NULL) == INVALID  # n % 32
+    assert g(A16, A16b, A16c, A16d, 4, 64, 40, A16, A16b, NULL) == INVALID  # k % 32
+    assert g(A16, A16b, A16c, A16d, 4, 64, 64, NULL, A16b, NULL) == INVALID
+    assert g(A16, A16b, A16c, A16d, 4, 64, 64, A16, MIS, NULL) == MISALIGNED
+    assert g(A16, NULL, A16c, A16d, 4, 64, 64, A16, A16b, NULL) == INVALID
+    assert g(NULL, NULL, NULL, NULL, 0, 64, 64, NULL, NULL, NULL) == SUCCESS
+
+
 def test_nv_quantize_validation(lib):
     q = lib.nvq_quantize
     assert q(A16, 1, 4, 24, A16b, 1, A16c, A16d, NULL) == INVALID

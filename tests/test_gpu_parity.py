@@ -552,6 +552,42 @@ def test_w4a4_full_size_sampled():
     say(f"C4: {len(rows)}x{len(cols)} sampled outputs, worst |err|/S {worst:.3g}")
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 32, 32), (70, 96, 160), (257, 160, 1056), (300, 704, 1024),
+                                   (777, 1056, 4096), (256, 512, 2048), (130, 32, 64)])
+def test_w4a4_quant_epilogue_matches_gemm_then_quantize(m, n, k):
+    """MXFP4 output from the epilogue == MXFP4 of the bf16 GEMM output, bit
+    for bit; and == the oracle's quantization of that bf16 product."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    qa, sa = mxq.quantize(dev(a))
+    qb, sb = mxq.quantize(dev(b))
+    cq, cs = mxq.gemm_w4a4_quant(qa, sa, qb, sb)
+    c = mxq.gemm_w4a4(qa, sa, qb, sb, torch.bfloat16)
+    q2, s2 = mxq.quantize(c)
+    assert np.array_equal(host(cs), host(s2)), f"{m}x{n}x{k}: scales differ from quantize(gemm)"
+    assert np.array_equal(host(cq), host(q2)), f"{m}x{n}x{k}: codes differ from quantize(gemm)"
+    qo, so = oracle.mx_quantize(host(c).view(np.uint16))
+    assert np.array_equal(host(cs), so) and np.array_equal(host(cq), qo), f"{m}x{n}x{k}: vs oracle"
+
+
+def test_w4a4_quant_full_size_and_empty_k():
+    a, b = w4a4_inputs()
+    qa, sa = mxq.quantize(dev(a))
+    qb, sb = mxq.quantize(dev(b))
+    cq, cs = mxq.gemm_w4a4_quant(qa, sa, qb, sb)
+    q2, s2 = mxq.quantize(mxq.gemm_w4a4(qa, sa, qb, sb, torch.bfloat16))
+    assert torch.equal(cq, q2) and torch.equal(cs, s2), "8192^3 epilogue quantize"
+    e = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
+    cq0 = torch.full((3, 32), 7, dtype=torch.uint8, device="cuda")
+    cs0 = torch.full((3, 2), 7, dtype=torch.uint8, device="cuda")
+    capi_rc = mxq.capi().mxq_gemm_w4a4_quant(mxq._p(e), mxq._p(e), mxq._p(e), mxq._p(e), 3, 64, 0, mxq._p(cq0),
+                                             mxq._p(cs0), mxq._stream())
+    assert capi_rc == 0
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(cq0).item() == 0 and torch.count_nonzero(cs0).item() == 0
+
+
 def test_products_with_empty_k_write_zeros():
     y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
     e = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
