@@ -50,6 +50,29 @@ __device__ __forceinline__ void store_mx_tile(const uint8_t* lo, const uint8_t* 
   }
 }
 
+// Stores a bf16 output tile staged in LDS (layout as in store_mx_tile) in
+// whole 16-byte units: consecutive threads write consecutive units of a
+// row.  A unit that crosses n (n % 8 != 0) is stored element by element.
+template <int ROWS, int COLS>
+__device__ __forceinline__ void store_bf16_tile(const uint8_t* lo, const uint8_t* hi, int64_t m0, int64_t n0,
+                                                int64_t m, int64_t n, uint16_t* __restrict__ c) {
+  constexpr int UNITS = COLS / 16;
+  for (int u = threadIdx.x; u < ROWS * UNITS; u += blockDim.x) {
+    const int r = u / UNITS, unit = u % UNITS;
+    const uint8_t* base = r < 128 ? lo : hi;
+    const u32x4 v = *(const u32x4*)(base + (r & 127) * COLS + ((unit ^ (r % UNITS)) << 4));
+    const int64_t gr = m0 + r, gc = n0 + 8 * unit;
+    if (gr >= m || gc >= n) continue;
+    uint16_t* dst = c + gr * n + gc;
+    if (gc + 8 <= n && (n & 7) == 0) {
+      *(u32x4*)dst = v;
+    } else {
+      const unsigned w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && gc + e < n; e++) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 // First version: every wave streams its own operand fragments from global
 // memory (L2-resident) -- block tile 128 x 128, wave tile 64 x 64 = 2 x 2
 // MFMAs per 64-wide k step.
@@ -423,10 +446,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   }
   wait_vmcnt<0>();  // no copy may still target LDS when the block ends
 
-  if constexpr (OUT == kOutMx) {
+  if constexpr (OUT == kOutMx || OUT == kOutBf16) {
     // the bf16 tile into the two code slots (idle now that every wave has
     // read its last fragments): rows 0..127 in slot 0, 128..255 in slot 1,
-    // 512 bytes per row, 16-byte unit u of row r at u ^ (r & 31)
+    // 512 bytes per row, 16-byte unit u of row r at u ^ (r & 31); then
+    // stored row by row in whole 16-byte units (bf16 output, a lane's own
+    // 8-byte pieces wrote partial lines) or quantized (MXFP4 output)
     __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     __syncthreads();
     uint8_t* lo = w4_codes<0>();
@@ -446,7 +471,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
         }
     }
     __syncthreads();
-    store_mx_tile<256, 512>(lo, hi, m0, n0, m, n, (uint8_t*)c, cs);
+    if constexpr (OUT == kOutMx)
+      store_mx_tile<256, 512>(lo, hi, m0, n0, m, n, (uint8_t*)c, cs);
+    else
+      store_bf16_tile<256, 512>(lo, hi, m0, n0, m, n, (uint16_t*)c);
     return;
   }
 
