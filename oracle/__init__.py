@@ -73,6 +73,10 @@ def _load():
     lib.or_nv_dequantize.argtypes = [P, P, ctypes.c_float, I64, I64, P]
     lib.or_gemm_nt.argtypes = [P, P, I64, I64, I64, P, P]
     lib.or_metrics.argtypes = [P, P, I64, P, P]
+    lib.or_e8m0_exponent_e4m3.argtypes = [ctypes.c_double]
+    lib.or_e8m0_exponent_e4m3.restype = I
+    lib.or_mx8_quantize.argtypes = [P, I, I64, I64, P, P]
+    lib.or_mx8_dequantize.argtypes = [P, P, I64, I64, P]
     lib.or_hadamard_norm.argtypes = [I]
     lib.or_hadamard_norm.restype = ctypes.c_float
     lib.or_hadamard_rotate.argtypes = [P, I, I64, I64, I, P]
@@ -153,6 +157,32 @@ def mx_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     assert s.shape == (rows, k // 32)
     y = np.empty((rows, k), dtype=np.float64)
     _load().or_mx_dequantize(_ptr(q), _ptr(s), rows, k, _ptr(y))
+    return y
+
+
+def e8m0_exponent_e4m3(amax: float) -> int:
+    """MXFP8 block exponent floor(log2 amax) - 8, clamped."""
+    return _load().or_e8m0_exponent_e4m3(float(amax))
+
+
+def mx8_quantize(x: np.ndarray):
+    """MXFP8: x[rows][k] -> (q[rows][k] E4M3 codes uint8, s[rows][k/32] E8M0)."""
+    x, dt = _as_input(x)
+    rows, k = x.shape
+    assert k % 32 == 0
+    q = np.empty((rows, k), dtype=np.uint8)
+    s = np.empty((rows, k // 32), dtype=np.uint8)
+    _load().or_mx8_quantize(_ptr(x), dt, rows, k, _ptr(q), _ptr(s))
+    return q, s
+
+
+def mx8_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    rows, k = q.shape
+    assert s.shape == (rows, k // 32)
+    y = np.empty((rows, k), dtype=np.float64)
+    _load().or_mx8_dequantize(_ptr(q), _ptr(s), rows, k, _ptr(y))
     return y
 
 

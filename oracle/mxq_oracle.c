@@ -239,6 +239,71 @@ void or_mx_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows,
 }
 
 /* ------------------------------------------------------------------ */
+/* MXFP8 (E4M3 elements, one E8M0 scale per 32)                        */
+/* ------------------------------------------------------------------ */
+
+/* MXFP8: FP8 values with one E8M0 scale per 1x32 block [GUIDE sec. 4.2
+ * table, the mxfp8 scheme]; used for activations next to MXFP4 weights
+ * [EXPLAINER, Kimi K3 release format].  The element is E4M3 (max 448 =
+ * 2^8 * 1.75, NaN only [GUIDE sec. 1.2]).  Block exponent by the same rule
+ * as MXFP4 with the element's top exponent: e = floor(log2 amax) - 8,
+ * clamped to [-127, 127] (amax = 0: -127), so the block's largest magnitude
+ * scales into [256, 512) and anything above 448 saturates; elements are
+ * E4M3(x * 2^-e) rounded to nearest even. */
+int or_e8m0_exponent_e4m3(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int ex;
+    frexp(amax, &ex); /* floor(log2 amax) = ex - 1 */
+    int e = (ex - 1) - 8;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+/* x[rows][k] -> q[rows][k] E4M3 codes, s[rows][k/32] E8M0 codes. */
+void or_mx8_quantize(const void *x, int dtype, int64_t rows, int64_t k,
+                     uint8_t *q, uint8_t *s)
+{
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            int64_t base = r * k + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; i++) {
+                double a = fabs((double)load_elem(x, dtype, base + i));
+                if (a > amax)
+                    amax = a;
+            }
+            int e = or_e8m0_exponent_e4m3(amax);
+            s[r * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; i++) {
+                /* x * 2^-e is exact in fp32 (a power-of-two scaling of an
+                 * fp32/bf16 value that stays below 512 in magnitude) */
+                float v = (float)ldexp((double)load_elem(x, dtype, base + i), -e);
+                q[base + i] = or_e4m3_encode(v);
+            }
+        }
+    }
+}
+
+/* Dequantize: x_hat = E4M3(c) * 2^(s - 127), exact in double. */
+void or_mx8_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows,
+                       int64_t k, double *y)
+{
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t i = 0; i < k; i++)
+            y[r * k + i] = or_e4m3_decode(q[r * k + i]) *
+                           or_e8m0_decode(s[r * nb + i / 32]);
+}
+
+/* ------------------------------------------------------------------ */
 /* NVFP4                                                               */
 /* ------------------------------------------------------------------ */
 

@@ -389,6 +389,54 @@ def test_table5_order_of_magnitude_diagnostic():
         assert abs(c - 1 / math.sqrt(1 + nm)) < 2e-3
 
 
+# ------------------------------------------------------------------ MXFP8
+
+def test_mx8_page_example_1_375_exact_with_unit_scale():
+    """With scale 1, E4M3 holds 1.375 exactly (infra-guide sec. 1.2); a block
+    whose largest magnitude is 448 = 1.75 * 2^8 takes e = 0 (code 127) and
+    stores 448 as 0x7E, 1.375 as 0x3B (S 0111 011), -0 as 0x80, 0.125 as 0x20."""
+    b = block_of([448.0, 1.375, -0.0, -1.375, 0.125])
+    q, s = oracle.mx8_quantize(b)
+    assert s[0, 0] == 127
+    assert list(q[0, :5]) == [0x7E, 0x3B, 0x80, 0xBB, 0x20]  # 0.125 = 2^(4 - 7): S 0100 000
+    assert np.array_equal(oracle.mx8_dequantize(q, s)[0, :5], [448.0, 1.375, 0.0, -1.375, 0.125])
+
+
+def test_mx8_exponent_rule_and_saturation():
+    """For a non-zero unclamped block the largest magnitude scales into
+    [256, 512) (floor(log2 amax) - 8), encodes to an E4M3 value >= 256 with
+    exponent field 15, and everything above 448 saturates to 448."""
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        e_true = int(rng.integers(-110, 110))
+        vals = (rng.standard_normal(32) * 2.0 ** e_true).astype(np.float32)
+        amax = float(np.max(np.abs(vals.astype(np.float64))))
+        e = oracle.e8m0_exponent_e4m3(amax)
+        assert e == math.floor(math.log2(amax)) - 8
+        assert 256.0 <= amax * 2.0 ** -e < 512.0
+        q, s = oracle.mx8_quantize(vals.reshape(1, 32))
+        assert s[0, 0] == e + 127
+        top = q[0, int(np.argmax(np.abs(vals)))] & 0x7F
+        assert (top >> 3) == 15 and top != 0x7F
+        d = np.abs(oracle.mx8_dequantize(q, s))
+        assert d.max() <= 448.0 * 2.0 ** e
+
+
+def test_mx8_all_finite_codes_roundtrip():
+    """Every finite E4M3 code times a power-of-two scale quantizes back to
+    itself when the block's largest element fixes the scale (idempotence)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for sc in (127, 100, 150):
+        vals = np.array([oracle.e4m3_decode(int(c)) for c in codes]) * 2.0 ** (sc - 127)
+        blocks = vals.reshape(-1, 2)  # 127 blocks of 2 codes, padded with the forcing element
+        x = np.zeros((blocks.shape[0], 32), dtype=np.float32)
+        x[:, 0] = 448.0 * 2.0 ** (sc - 127)
+        x[:, 1:3] = blocks
+        q, s = oracle.mx8_quantize(x)
+        assert np.all(s == sc)
+        assert np.array_equal(q[:, 1:3].reshape(-1), codes)
+
+
 # ------------------------------------------------------------------ block Hadamard rotation
 
 def _nearest_f32(exact):
