@@ -9,7 +9,8 @@ already resident in HBM:
          with the 32-point block Hadamard rotation fused ahead of it
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
-         (bf16 output, and MXFP4 output quantized in the epilogue)
+         (bf16 output, and MXFP4 output quantized in the epilogue); MXFP8
+         quantize of the same A + W4A8 GEMM 8192^3 (E4M3 x E2M1 MFMA)
   c5     NVFP4 and MXFP4 quantize of W 8192x4096 and X 4096x4096, and the
          W4A16 GEMM Y = X W^T (4096x8192x4096) in each format
 Every HBM-bound op cycles through copies of its operands whose combined size
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA; an E4M3 x E2M1 product issues at this rate
 BURST = 16  # launches per event pair in the kernel-rate region
 COLD_BYTES = 768 << 20  # rotation set size for HBM-bound ops (3x the 256 MB cache)
 BF16_PEAK_TFLOPS = 2500.0
@@ -178,6 +180,15 @@ def main():
         cs4 = torch.empty((8192, 256), dtype=u8, device=dev)
         ops.append(("gemm_w4a4_8192_mxfp4_out", lambda: mxq.gemm_w4a4_quant(qa4, sa4, qb4, sb4, cq4, cs4),
                     3 * mx_bytes(8192, 8192), 2 * 8192 ** 3))
+        # MXFP8 activations (E4M3 + E8M0 per 32) against the same MXFP4 weights
+        qa8 = torch.empty((8192, 8192), dtype=u8, device=dev)
+        sa8 = torch.empty((8192, 256), dtype=u8, device=dev)
+        sets8 = [(a4d if c == 0 else sets[c][0], qa8 if c == 0 else torch.empty_like(qa8),
+                  sa8 if c == 0 else torch.empty_like(sa8)) for c in range(na)]
+        ops.append(("quantize_fp8_a_8192x8192_bf16", rotating(sets8, lambda x, q, s: mxq.quantize_fp8(x, q, s)),
+                    8192 * 8192 * 3 + 8192 * 256, 0))
+        ops.append(("gemm_w4a8_8192", lambda: mxq.gemm_w4a8(qa8, sa8, qb4, sb4, c=c4),
+                    8192 * 8192 + 8192 * 256 + mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3))
     if "c5" in parts:
         w5, x5 = synth.nv_vs_mx()
         w5d, x5d = to_dev(w5), to_dev(x5)
@@ -283,6 +294,8 @@ def main():
             a, p, u = r["GB/s"], HBM_PEAK_GBS, "GB/s"
         elif bound == "mfma_fp4":
             a, p, u = r["TFLOP/s"], FP4_PEAK_TFLOPS, "TFLOP/s"
+        elif bound == "mfma_fp8":
+            a, p, u = r["TFLOP/s"], FP8_PEAK_TFLOPS, "TFLOP/s"
         else:
             a, p, u = r["TFLOP/s"], BF16_PEAK_TFLOPS, "TFLOP/s"
         out = {"bound": "hbm" if bound == "hbm" else "mfma", "achieved": a, "peak": p, "unit": u,
@@ -293,6 +306,8 @@ def main():
     for name in per_op:
         if name.startswith("gemm_w4a4"):  # both output kinds
             rooflines[name] = roof(name, "mfma_fp4")
+        elif name.startswith("gemm_w4a8"):
+            rooflines[name] = roof(name, "mfma_fp8")
         elif "gemm_w4a16_4096" in name:
             rooflines[name] = roof(name, "mfma_bf16")
         else:

@@ -122,6 +122,19 @@ MXQ_API mxq_status mxq_quantize_hadamard(const void *x, mxq_dtype xdt, int64_t r
                                  hipStream_t stream);
 
 /*
+ * MXFP8 quantize.  x[rows][k] (xdt) -> q[rows][k] E4M3 codes (one byte per
+ * element) and s[rows][k/32] E8M0 scale codes.  Block exponent e =
+ * floor(log2 amax) - 8, clamped to [-127, 127] (448 = 1.75 * 2^8 is E4M3's
+ * largest value, so the block's largest magnitude scales into [256, 512));
+ * elements E4M3(x * 2^-e), round to nearest even, saturating at 448, sign
+ * of zero kept.  k % 32 == 0.  [infra-guide "4.5 FP8 and NVFP4/MXFP4" sec.
+ * 4.2: the mxfp8 scheme, FP8 values with an E8M0 scale per 1x32; sec. 1.2:
+ * E4M3 range and NaN-only special value.]  Errors as mxq_quantize.
+ */
+MXQ_API mxq_status mxq_quantize_fp8(const void *x, mxq_dtype xdt, int64_t rows, int64_t k,
+                            uint8_t *q, uint8_t *s, hipStream_t stream);
+
+/*
  * MXFP4 dequantize.  (q[rows][k/2], s[rows][k/32]) -> y[rows][k] of type ydt:
  * y = E2M1(code) * 2^(s - 127), exact in fp32 and bf16 for scale codes
  * 1..250 [TransFP4 page eq. (1) with s_g = 1].  Scale code 255 (NaN in E8M0)
@@ -153,6 +166,20 @@ MXQ_API mxq_status mxq_gemv_w4a16(const uint8_t *wq, const uint8_t *ws, int64_t 
  * sec. 5.1].  k % 32 == 0.
  */
 MXQ_API mxq_status mxq_gemm_w4a4(const uint8_t *aq, const uint8_t *as,
+                         const uint8_t *bq, const uint8_t *bs, int64_t m,
+                         int64_t n, int64_t k, void *c, mxq_dtype cdt,
+                         hipStream_t stream);
+
+/*
+ * W4A8 product: c[m][n] = sum_k A_hat[m][k] * B_hat[n][k] with MXFP8
+ * activations A = (aq8[m][k] E4M3, as[m][k/32]) and MXFP4 weights
+ * B = (bq[n][k/2], bs[n][k/32]), on the block-scaled MFMA that takes an
+ * E4M3 and an E2M1 operand; fp32 accumulation; c written as cdt.  k % 32 ==
+ * 0.  [Kimi K3 release format: MXFP4 weights with MXFP8 activations, "Low-
+ * precision inference and MXFP4 quantization" page; mxfp8 scheme, infra-
+ * guide sec. 4.2.]  Errors as mxq_gemm_w4a4.
+ */
+MXQ_API mxq_status mxq_gemm_w4a8(const uint8_t *aq8, const uint8_t *as,
                          const uint8_t *bq, const uint8_t *bs, int64_t m,
                          int64_t n, int64_t k, void *c, mxq_dtype cdt,
                          hipStream_t stream);

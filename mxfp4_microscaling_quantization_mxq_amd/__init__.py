@@ -32,8 +32,9 @@ STATUS = {
     4: "MXQ_ERROR_LAUNCH_FAILURE",
 }
 API = (
-    "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_dequantize",
-    "mxq_gemv_w4a16", "mxq_gemm_w4a4", "mxq_gemm_w4a4_quant", "nvq_quantize", "nvq_dequantize", "nvq_gemm",
+    "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_quantize_fp8",
+    "mxq_dequantize", "mxq_gemv_w4a16", "mxq_gemm_w4a4", "mxq_gemm_w4a4_quant", "mxq_gemm_w4a8",
+    "nvq_quantize", "nvq_dequantize", "nvq_gemm",
 )
 
 
@@ -64,6 +65,8 @@ def capi() -> ctypes.CDLL:
     lib.mxq_version.restype = I
     lib.mxq_quantize.argtypes = [P, I, I64, I64, P, P, P]
     lib.mxq_quantize_hadamard.argtypes = [P, I, I64, I64, I, P, P, P]
+    lib.mxq_quantize_fp8.argtypes = [P, I, I64, I64, P, P, P]
+    lib.mxq_gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
     lib.mxq_dequantize.argtypes = [P, P, I64, I64, P, I, P]
     lib.mxq_gemv_w4a16.argtypes = [P, P, I64, I64, P, I64, P, I, P]
     lib.mxq_gemm_w4a4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
@@ -153,6 +156,19 @@ def quantize_hadamard(x, hk=32, q=None, s=None):
     return q, s
 
 
+def quantize_fp8(x, q=None, s=None):
+    """MXFP8 quantize x[rows, k] -> (q[rows, k] E4M3 codes u8, s[rows, k/32] E8M0 u8)."""
+    torch = _torch()
+    _need(x, "x")
+    rows, k = x.shape
+    if q is None:
+        q = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _check(capi().mxq_quantize_fp8(_p(x), _dtype_code(x.dtype), rows, k, _p(q), _p(s), _stream()), "mxq_quantize_fp8")
+    return q, s
+
+
 def dequantize(q, s, dtype=None, y=None):
     """(q[rows, k/2], s[rows, k/32]) -> y[rows, k] in dtype (default bf16)."""
     torch = _torch()
@@ -198,6 +214,23 @@ def gemm_w4a4(aq, as_, bq, bs, out_dtype=None, c=None):
         c = torch.empty((m, n), dtype=out_dtype, device=aq.device)
     _check(capi().mxq_gemm_w4a4(_p(aq), _p(as_), _p(bq), _p(bs), m, n, k, _p(c), _dtype_code(c.dtype), _stream()),
            "mxq_gemm_w4a4")
+    return c
+
+
+def gemm_w4a8(aq8, as_, bq, bs, out_dtype=None, c=None):
+    """c[m, n] = deq8(A)[m, k] @ deq4(B)[n, k]^T: MXFP8 activations, MXFP4 weights."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    for t, nm in ((aq8, "aq8"), (as_, "as"), (bq, "bq"), (bs, "bs")):
+        _need(t, nm, torch.uint8)
+    m, k = aq8.shape
+    n = bq.shape[0]
+    if bq.shape[1] * 2 != k:
+        raise ValueError("A and B disagree on k")
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=aq8.device)
+    _check(capi().mxq_gemm_w4a8(_p(aq8), _p(as_), _p(bq), _p(bs), m, n, k, _p(c), _dtype_code(c.dtype), _stream()),
+           "mxq_gemm_w4a8")
     return c
 
 

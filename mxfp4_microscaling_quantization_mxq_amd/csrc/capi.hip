@@ -93,6 +93,18 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype xdt, int64_t rows, int
   return launched(mxq::launch_mx_quantize_hadamard(x, xdt == MXQ_BF16, rows, k, hk, q, s, stream));
 }
 
+mxq_status mxq_quantize_fp8(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
+                            hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
+  if (!x || !q || !s) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_mx8_quantize(x, xdt == MXQ_BF16, rows, k, q, s, stream));
+}
+
 mxq_status mxq_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y, mxq_dtype ydt,
                           hipStream_t stream) {
   if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
@@ -153,6 +165,25 @@ mxq_status mxq_gemm_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
   return launched(mxq::launch_w4a4(aq, as, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
+}
+
+mxq_status mxq_gemm_w4a8(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                         int64_t n, int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return MXQ_SUCCESS;
+  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (!c) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
+  if (k == 0) {
+    mxq_status d = check_device();
+    if (d != MXQ_SUCCESS) return d;
+    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
+  }
+  if (!aq8 || !as || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(aq8) || !aligned16(as) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_w4a8(aq8, as, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
 }
 
 mxq_status mxq_gemm_w4a4_quant(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,

@@ -10,6 +10,13 @@ namespace mxq {
 
 hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
                               hipStream_t st);
+// MXFP8: q[rows][k] E4M3 codes, s[rows][k/32] E8M0 codes.
+hipError_t launch_mx8_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
+                               hipStream_t st);
+// W4A8: c[m][n] = sum_k A8_hat[m][k] * B4_hat[n][k], A MXFP8 (aq8[m][k],
+// as[m][k/32]), B MXFP4; fp32 accumulation; c as fp32 or bf16.
+hipError_t launch_w4a8(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
 // MXFP4 of x rotated block by block along k with the orthonormal Hadamard
 // H_hk, hk in {16, 32, 64, 128}, k % max(32, hk) == 0.
 hipError_t launch_mx_quantize_hadamard(const void* x, bool bf16, int64_t rows, int64_t k, int hk, uint8_t* q,

@@ -85,6 +85,80 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restric
   }
 }
 
+// ---------------------------------------------------------------- MXFP8
+
+// MXFP8: E4M3 elements with one E8M0 scale per 32 [infra-guide "4.5 FP8 and
+// NVFP4/MXFP4", sec. 4.2: the mxfp8 scheme, FP8 values and an E8M0 scale
+// per 1x32; sec. 1.2: E4M3, max 448, NaN only].  Block exponent by the
+// MXFP4 rule with E4M3's top exponent: code = max(expfield(amax) - 8, 0),
+// i.e. floor(log2 amax) - 8 + 127, so the block's largest magnitude scales
+// into [256, 512).  Elements: the gfx950 scaled fp8 convert (round to
+// nearest even), after clamping every magnitude to 448 * 2^e: the convert
+// itself turns scaled values past 448 into the NaN code instead of
+// saturating (seen in the bit-exact comparison with the CPU oracle), and the
+// clamp is exact (448 * 2^e is a bf16 / fp32 number, and x * 2^-e is exact).
+// One lane = 8 elements, a quad = one block; a lane stores 8 code bytes.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned e8m0_code_e4m3(unsigned ef) { return ef > 8u ? ef - 8u : 0u; }
+
+__global__ __launch_bounds__(256) void k_mx8_quantize_bf16(const u32x4* __restrict__ x, u32x2* __restrict__ q,
+                                                           uint8_t* __restrict__ s, int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;  // quads stay whole
+  const bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
+  const u32x4 v = __builtin_bit_cast(u32x4, xb);
+  unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
+  m = max(m & 0xFFFFu, m >> 16);
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  const unsigned code = e8m0_code_e4m3(m >> 7);
+  const float scale = e8m0_as_scale(code);
+  // |x| clamped to 448 * 2^e (bf16 bits: exponent field code + 8, mantissa
+  // .11), sign kept
+  const unsigned lim = ((code + 8u) << 7) | 0x60u;
+  const u16x2 lim2 = {(unsigned short)lim, (unsigned short)lim};
+  u32x4 cl;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const unsigned w = v[i];
+    const u16x2 mg = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+    cl[i] = __builtin_bit_cast(unsigned, __builtin_elementwise_min(mg, lim2)) | (w & 0x80008000u);
+  }
+  const bf16x8 xc = __builtin_bit_cast(bf16x8, cl);
+  s16x2 lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[0], xc[1]}, scale, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[2], xc[3]}, scale, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[4], xc[5]}, scale, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[6], xc[7]}, scale, true);
+  q[t] = (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+}
+
+__global__ __launch_bounds__(256) void k_mx8_quantize_f32(const u32x4* __restrict__ x, u32x2* __restrict__ q,
+                                                          uint8_t* __restrict__ s, int64_t nlanes) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;
+  const u32x4 a = __builtin_nontemporal_load(&x[2 * t]);
+  const u32x4 b = __builtin_nontemporal_load(&x[2 * t + 1]);
+  unsigned m = max(max(max(a.x & 0x7FFFFFFFu, a.y & 0x7FFFFFFFu), max(a.z & 0x7FFFFFFFu, a.w & 0x7FFFFFFFu)),
+                   max(max(b.x & 0x7FFFFFFFu, b.y & 0x7FFFFFFFu), max(b.z & 0x7FFFFFFFu, b.w & 0x7FFFFFFFu)));
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  const unsigned code = e8m0_code_e4m3(m >> 23);
+  const float scale = e8m0_as_scale(code);
+  // |x| clamped to 448 * 2^e (fp32 bits: exponent field code + 8, mantissa .11)
+  const unsigned lim = ((code + 8u) << 23) | 0x600000u;
+  auto clamp = [&](unsigned w) { return __uint_as_float(min(w & 0x7FFFFFFFu, lim) | (w & 0x80000000u)); };
+  s16x2 lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, clamp(a.x), clamp(a.y), scale, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, clamp(a.z), clamp(a.w), scale, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, clamp(b.x), clamp(b.y), scale, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, clamp(b.z), clamp(b.w), scale, true);
+  q[t] = (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+}
+
 // ---------------------------------------------------------------- rotated MXFP4
 
 // Block Hadamard rotation fused ahead of the MXFP4 quantizer: y_j = H x_j
@@ -380,6 +454,18 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
   else
     hipLaunchKernelGGL(k_mx_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
                        (unsigned*)q, s, nlanes);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx8_quantize(const void* x, bool bf16, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
+                               hipStream_t st) {
+  const int64_t nlanes = rows * k / 8;
+  if (bf16)
+    hipLaunchKernelGGL(k_mx8_quantize_bf16, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (u32x2*)q, s, nlanes);
+  else
+    hipLaunchKernelGGL(k_mx8_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (u32x2*)q, s, nlanes);
   return hipGetLastError();
 }
 

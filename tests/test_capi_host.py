@@ -81,6 +81,19 @@ def test_quantize_hadamard_validation(lib):
     assert q(NULL, 1, 0, 64, 32, NULL, NULL, NULL) == SUCCESS  # empty
 
 
+def test_quantize_fp8_and_w4a8_validation(lib):
+    q = lib.mxq_quantize_fp8
+    assert q(A16, 1, 4, 48, A16b, A16c, NULL) == INVALID  # k % 32
+    assert q(A16, 1, 4, 32, NULL, A16c, NULL) == INVALID
+    assert q(A16, 1, 4, 32, MIS, A16c, NULL) == MISALIGNED
+    assert q(NULL, 1, 0, 32, NULL, NULL, NULL) == SUCCESS
+    g = lib.mxq_gemm_w4a8
+    assert g(A16, A16b, A16c, A16d, 4, 4, 33, A16, 1, NULL) == INVALID
+    assert g(A16, A16b, A16c, NULL, 4, 4, 32, A16, 1, NULL) == INVALID
+    assert g(A16, A16b, A16c, A16d, 4, 4, 32, MIS, 1, NULL) == MISALIGNED
+    assert g(NULL, NULL, NULL, NULL, 0, 4, 32, NULL, 1, NULL) == SUCCESS
+
+
 def test_dequantize_validation(lib):
     d = lib.mxq_dequantize
     assert d(A16, A16b, 4, 40, A16c, 1, NULL) == INVALID
