@@ -230,7 +230,7 @@ def w4a8_case(a_np, b_np, what, dts=None, exact_groups=False):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (31, 33, 64), (70, 90, 160), (200, 130, 1056), (257, 129, 96),
-                                   (300, 700, 1024), (256, 512, 2048)])
+                                   (300, 700, 1024), (256, 512, 2048), (1, 300, 1024), (129, 257, 3072)])
 def test_w4a8_ragged(m, n, k):
     rng = np.random.default_rng(m * 7 + n + k)
     a = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * np.exp2(rng.integers(-6, 7, size=(m, 1)))).astype(np.float32))
@@ -238,7 +238,8 @@ def test_w4a8_ragged(m, n, k):
     w4a8_case(a, b, f"w4a8 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (31, 33, 64), (70, 90, 160), (257, 129, 96), (300, 700, 1024)])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (31, 33, 64), (70, 90, 160), (257, 129, 96), (300, 700, 1024),
+                                   (129, 257, 2048)])
 def test_w4a8_one_term_per_group(m, n, k):
     """Activations with one nonzero per 8 consecutive k (random place, sign,
     magnitude and per-row range): every group sum is exact, so any slip in
