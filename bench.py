@@ -357,8 +357,8 @@ def _src_digest(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"gemv": ["w4a16.hip", "mxq_device.h"], "w4a4": ["w4a4.hip", "mxq_device.h"],
-                  "quantize": ["quant.hip", "mxq_device.h"]}
+KERNEL_SOURCES = {"gemv": ["w4a16.hip", "mxq_device.h"], "w4a4": ["w4a4.hip", "mxq_device.h", "mxq_gemm_common.h"],
+                  "w4a8": ["w4a8.hip", "mxq_device.h", "mxq_gemm_common.h"], "quantize": ["quant.hip", "mxq_device.h"]}
 
 
 def traffic_for(name):
