@@ -80,6 +80,14 @@ def _load():
     lib.or_hadamard_norm.argtypes = [I]
     lib.or_hadamard_norm.restype = ctypes.c_float
     lib.or_hadamard_rotate.argtypes = [P, I, I64, I64, I, P]
+    lib.or_int4_decode.argtypes = [ctypes.c_uint8]
+    lib.or_int4_decode.restype = ctypes.c_double
+    lib.or_int4_encode.argtypes = [ctypes.c_double]
+    lib.or_int4_encode.restype = ctypes.c_uint8
+    lib.or_tf4_encode_rotated.argtypes = [P, I64, I64, P, I, P, P, P, P]
+    lib.or_tf4_quantize.argtypes = [P, I, I64, I64, P, I, P, P, P, P]
+    lib.or_tf4_decode_rotated.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, P]
+    lib.or_tf4_dequantize.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, P]
     _lib = lib
     return lib
 
@@ -238,6 +246,82 @@ def hadamard_rotate(x: np.ndarray, hk: int) -> np.ndarray:
 def mx_quantize_hadamard(x: np.ndarray, hk: int = 32):
     """Rotated MXFP4: MXFP4 codes and scales of hadamard_rotate(x, hk)."""
     return mx_quantize(hadamard_rotate(x, hk))
+
+
+def int4_decode(code: int) -> float:
+    """Sign-magnitude INT4 code -> value in {-7..7}."""
+    return _load().or_int4_decode(code)
+
+
+def int4_encode(v: float) -> int:
+    """Nearest INT4 magnitude (ties to even), saturating at 7, sign kept."""
+    return _load().or_int4_encode(float(v))
+
+
+def _tf4_outputs(rows, k):
+    return (np.empty((rows, k // 2), dtype=np.uint8), np.empty((rows, k // 16), dtype=np.uint8),
+            np.empty((rows, k // 32), dtype=np.uint8), np.empty((rows, k // 32), dtype=np.uint16))
+
+
+def tf4_encode_rotated(y: np.ndarray, gscale: float | None = None):
+    """TransFP4 encode of already rotated fp32 values y[rows][k]:
+    (q, s E4M3 [rows][k/16], meta [rows][k/32], res bf16 bits [rows][k/32], s_t)
+    [TransFP4 page sec. 2.3 eq. (3), sec. 3.1]."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    rows, k = y.shape
+    assert k % 32 == 0
+    q, s, meta, res = _tf4_outputs(rows, k)
+    g = np.zeros(1, dtype=np.float32)
+    compute = gscale is None
+    if not compute:
+        g[0] = np.float32(gscale)
+    _load().or_tf4_encode_rotated(_ptr(y), rows, k, _ptr(g), int(compute), _ptr(q), _ptr(s), _ptr(meta),
+                                  _ptr(res))
+    return q, s, meta, res, float(g[0])
+
+
+def tf4_quantize(x: np.ndarray, gscale: float | None = None):
+    """TransFP4 quantize of x[rows][k]: 32-point Hadamard, one bf16 residual
+    per 32, per-block NVFP4-or-INT4 codes under E4M3 scales and s_t."""
+    x, dt = _as_input(x)
+    rows, k = x.shape
+    assert k % 32 == 0
+    q, s, meta, res = _tf4_outputs(rows, k)
+    g = np.zeros(1, dtype=np.float32)
+    compute = gscale is None
+    if not compute:
+        g[0] = np.float32(gscale)
+    _load().or_tf4_quantize(_ptr(x), dt, rows, k, _ptr(g), int(compute), _ptr(q), _ptr(s), _ptr(meta), _ptr(res))
+    return q, s, meta, res, float(g[0])
+
+
+def _tf4_inputs(q, s, meta, res):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows, half = q.shape
+    k = 2 * half
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    res = np.ascontiguousarray(res, dtype=np.uint16)
+    assert s.shape == (rows, k // 16) and meta.shape == (rows, k // 32) and res.shape == (rows, k // 32)
+    return q, s, meta, res, rows, k
+
+
+def tf4_decode_rotated(q, s, meta, res, gscale: float) -> np.ndarray:
+    """Rotated-domain reconstruction (fp32): codes times block scales, plus
+    the residual at its position."""
+    q, s, meta, res, rows, k = _tf4_inputs(q, s, meta, res)
+    y = np.empty((rows, k), dtype=np.float32)
+    _load().or_tf4_decode_rotated(_ptr(q), _ptr(s), _ptr(meta), _ptr(res), float(np.float32(gscale)), rows, k,
+                                  _ptr(y))
+    return y
+
+
+def tf4_dequantize(q, s, meta, res, gscale: float) -> np.ndarray:
+    """x_hat = H^T y_hat per 32-block, fp32 (eq. (3))."""
+    q, s, meta, res, rows, k = _tf4_inputs(q, s, meta, res)
+    y = np.empty((rows, k), dtype=np.float32)
+    _load().or_tf4_dequantize(_ptr(q), _ptr(s), _ptr(meta), _ptr(res), float(np.float32(gscale)), rows, k, _ptr(y))
+    return y
 
 
 def gemm_nt(a: np.ndarray, b: np.ndarray):

@@ -38,6 +38,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define OR_F32 0
@@ -441,6 +442,226 @@ void or_hadamard_rotate(const void *x, int dtype, int64_t rows, int64_t k,
             fwht_block_f32(v, hk);
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* TransFP4 blocks: rotation + sparse residual + FP4/INT4 choice        */
+/* ------------------------------------------------------------------ */
+
+/* [TRANSFP4 sec. 2.3 eq. (3)]: x_hat_j = H^T Q_f(H x_j - P_r H x_j)
+ * + H^T P_r H x_j, where P_r keeps r positions of the rotated block in a
+ * separate higher-precision residual stream; [TRANSFP4 sec. 3.1]: a 32-point
+ * Hadamard, at most one residual per 32 values, and per block the NVFP4 or
+ * the INT4 candidate, whichever has the smaller block error; [TRANSFP4 sec.
+ * 2.2 Table 3]: the residual lane keeps one 16-bit value per 32; the format
+ * tag selects the element codebook (E2M1 or INT4).
+ *
+ * Readings (the page leaves them open; listed in the design notes):
+ *   - rotation: H_32 exactly as or_hadamard_rotate (fp32 butterfly order);
+ *   - residual: the position of the largest |y_i| (lowest index on ties),
+ *     value rounded to bf16 (nearest even); that position is set to +0 in
+ *     the block the codebook quantizes;
+ *   - both candidates use the NVFP4 two-level scale: one E4M3 scale per 16
+ *     under the fp32 tensor scale s_t = amax'/2688 (amax' over the rotated,
+ *     residual-free tensor); the NVFP4 candidate maps the 16-block amax to
+ *     E2M1's 6, the INT4 candidate to 7, with the same fp32 order as
+ *     or_nv_quantize (t = fl(Q s_t), s_b = E4M3(fl(amax/t)),
+ *     d = fl(s_t E4M3(s_b)), v = fl(y/d));
+ *   - INT4: sign and magnitude, magnitudes 0..7, round half to even,
+ *     saturating at 7 (code = sign << 3 | magnitude, like E2M1's layout);
+ *   - block error: SSE = sum of fl(e_i * e_i), e_i = fl(y_i - fl(c_i d)),
+ *     summed in fp32 as four sequential runs of 8 (elements 8l..8l+7), then
+ *     (P0 + P1) + (P2 + P3); INT4 wins only if its SSE is strictly smaller;
+ *   - storage per 32-block: 16 code bytes, two E4M3 scale bytes, one meta
+ *     byte (bit 7 = INT4 tag, bits 0-4 = residual position), one bf16. */
+
+double or_int4_decode(uint8_t code)
+{
+    double m = (double)(code & 7);
+    return (code & 8) ? -m : m;
+}
+
+uint8_t or_int4_encode(double v)
+{
+    double a = fabs(v);
+    double n = floor(a);
+    double f = a - n;
+    if (f > 0.5 || (f == 0.5 && fmod(n, 2.0) == 1.0))
+        n += 1.0;
+    if (n > 7.0)
+        n = 7.0;
+    return (uint8_t)((signbit(v) ? 8 : 0) | (int)n);
+}
+
+static uint16_t f32_to_bf16_bits_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static float bf16_bits_to_f32(uint16_t b) { return bf16_to_f32(b); }
+
+/* One candidate for a 32-block of residual-free rotated values yp[32]:
+ * qmax = 6 (E2M1) or 7 (INT4).  Writes codes[32], sb[2]; returns the SSE. */
+static float tf4_candidate(const float *yp, float st, int int4, uint8_t *codes,
+                           uint8_t *sb)
+{
+    const float t = (int4 ? 7.0f : 6.0f) * st;
+    float err[32];
+    for (int h = 0; h < 2; h++) {
+        float amax = 0.0f;
+        for (int i = 0; i < 16; i++) {
+            float a = fabsf(yp[16 * h + i]);
+            if (a > amax)
+                amax = a;
+        }
+        uint8_t sc = or_e4m3_encode(amax / t);
+        sb[h] = sc;
+        float sv = (float)or_e4m3_decode(sc);
+        float d = st * sv;
+        for (int i = 16 * h; i < 16 * h + 16; i++) {
+            uint8_t c;
+            float dq;
+            if (sv == 0.0f) {
+                c = (uint8_t)(signbit(yp[i]) ? 8 : 0);
+                dq = 0.0f;
+            } else {
+                float v = yp[i] / d;
+                c = int4 ? or_int4_encode((double)v) : or_e2m1_encode((double)v, 0);
+                float cv = (float)(int4 ? or_int4_decode(c) : or_e2m1_decode(c));
+                dq = cv * d;
+            }
+            codes[i] = c;
+            err[i] = yp[i] - dq;
+        }
+    }
+    float part[4];
+    for (int l = 0; l < 4; l++) {
+        float acc = 0.0f;
+        for (int i = 8 * l; i < 8 * l + 8; i++) {
+            float sq = err[i] * err[i];
+            acc = acc + sq;
+        }
+        part[l] = acc;
+    }
+    float a01 = part[0] + part[1];
+    float a23 = part[2] + part[3];
+    return a01 + a23;
+}
+
+/* Residual step on one rotated block: position of the largest |y| (lowest
+ * index on ties), its bf16 value, and the residual-free block. */
+static int tf4_split(const float *y, float *yp, uint16_t *res)
+{
+    int at = 0;
+    float best = fabsf(y[0]);
+    for (int i = 1; i < 32; i++)
+        if (fabsf(y[i]) > best) {
+            best = fabsf(y[i]);
+            at = i;
+        }
+    for (int i = 0; i < 32; i++)
+        yp[i] = y[i];
+    *res = f32_to_bf16_bits_rne(y[at]);
+    yp[at] = 0.0f;
+    return at;
+}
+
+/* Encode rotated values y[rows][k] (fp32, k % 32 == 0) with tensor scale
+ * *gscale (computed from the residual-free values when compute_gscale != 0).
+ * Outputs q[rows][k/2], s[rows][k/16] E4M3, meta[rows][k/32],
+ * res[rows][k/32] bf16 bits. */
+void or_tf4_encode_rotated(const float *y, int64_t rows, int64_t k, float *gscale,
+                           int compute_gscale, uint8_t *q, uint8_t *s,
+                           uint8_t *meta, uint16_t *res)
+{
+    const int64_t nb = k / 32;
+    if (compute_gscale) {
+        float amax = 0.0f;
+        for (int64_t r = 0; r < rows; r++)
+            for (int64_t b = 0; b < nb; b++) {
+                float yp[32];
+                uint16_t rv;
+                tf4_split(y + r * k + b * 32, yp, &rv);
+                for (int i = 0; i < 32; i++)
+                    if (fabsf(yp[i]) > amax)
+                        amax = fabsf(yp[i]);
+            }
+        *gscale = or_nv_tensor_scale(amax);
+    }
+    const float st = *gscale;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float yp[32];
+            uint16_t rv;
+            int at = tf4_split(y + r * k + b * 32, yp, &rv);
+            uint8_t cn[32], ci[32], sn[2], si[2];
+            float en = tf4_candidate(yp, st, 0, cn, sn);
+            float ei = tf4_candidate(yp, st, 1, ci, si);
+            int use_int4 = ei < en;
+            const uint8_t *c = use_int4 ? ci : cn;
+            const uint8_t *sc = use_int4 ? si : sn;
+            for (int j = 0; j < 16; j++)
+                q[r * (k / 2) + b * 16 + j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+            s[r * (k / 16) + 2 * b] = sc[0];
+            s[r * (k / 16) + 2 * b + 1] = sc[1];
+            meta[r * nb + b] = (uint8_t)((use_int4 ? 0x80 : 0) | at);
+            res[r * nb + b] = rv;
+        }
+    }
+}
+
+/* TransFP4 quantize of x[rows][k] (dtype): rotate with H_32, then encode. */
+void or_tf4_quantize(const void *x, int dtype, int64_t rows, int64_t k, float *gscale,
+                     int compute_gscale, uint8_t *q, uint8_t *s, uint8_t *meta,
+                     uint16_t *res)
+{
+    float *y = (float *)malloc((size_t)(rows * k) * sizeof(float));
+    or_hadamard_rotate(x, dtype, rows, k, 32, y);
+    or_tf4_encode_rotated(y, rows, k, gscale, compute_gscale, q, s, meta, res);
+    free(y);
+}
+
+/* Rotated-domain reconstruction yh[rows][k] (fp32): y_hat_i = fl(c_i * d_h)
+ * with d_h = fl(s_t * E4M3(s_h)) and the codebook the tag selects, plus the
+ * bf16 residual at its position (whose code is zero). */
+void or_tf4_decode_rotated(const uint8_t *q, const uint8_t *s, const uint8_t *meta,
+                           const uint16_t *res, float gscale, int64_t rows, int64_t k,
+                           float *yh)
+{
+    const int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t m = meta[r * nb + b];
+            const int int4 = (m & 0x80) != 0, at = m & 31;
+            float *v = yh + r * k + b * 32;
+            for (int i = 0; i < 32; i++) {
+                uint8_t byte = q[r * (k / 2) + b * 16 + i / 2];
+                uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
+                float d = gscale * (float)or_e4m3_decode(s[r * (k / 16) + 2 * b + i / 16]);
+                float cv = (float)(int4 ? or_int4_decode(c) : or_e2m1_decode(c));
+                v[i] = cv * d;
+            }
+            v[at] = v[at] + bf16_bits_to_f32(res[r * nb + b]);
+        }
+    }
+}
+
+/* TransFP4 dequantize: x_hat = H^T y_hat per block (H_32 is symmetric and
+ * orthonormal, so H^T = H; same fp32 butterfly as the forward rotation). */
+void or_tf4_dequantize(const uint8_t *q, const uint8_t *s, const uint8_t *meta,
+                       const uint16_t *res, float gscale, int64_t rows, int64_t k,
+                       float *xh)
+{
+    or_tf4_decode_rotated(q, s, meta, res, gscale, rows, k, xh);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < k / 32; b++)
+            fwht_block_f32(xh + r * k + b * 32, 32);
 }
 
 /* ------------------------------------------------------------------ */
