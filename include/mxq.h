@@ -235,6 +235,48 @@ MXQ_API mxq_status nvq_gemm(const uint8_t *wq, const uint8_t *ws, const float *w
                     int64_t n, int64_t k, const void *x, int64_t m, void *y,
                     mxq_dtype ydt, hipStream_t stream);
 
+/*
+ * TransFP4 quantize [TransFP4 page sec. 2.3 eq. (3): x_hat = H^T Q_f(Hx -
+ * P_r Hx) + H^T P_r Hx; sec. 3.1: 32-point Hadamard, at most one residual
+ * per 32 values, per-block choice between the NVFP4 and the INT4 candidate
+ * by block error; sec. 2.2 Table 3: a 16-bit residual lane and a format
+ * tag].  Per 32-element block of x[rows][k] (xdt) along k:
+ *   - y = H_32 x in fp32 (the order of mxq_quantize_hadamard);
+ *   - the residual: the position of the largest |y_i| (first on ties) and
+ *     that value rounded to bf16; the position is set to +0;
+ *   - candidates under one E4M3 scale per 16 and the fp32 tensor scale s_t:
+ *     E2M1 codes (16-block amax mapped to 6) or INT4 codes (sign and
+ *     magnitude 0..7, nearest even, amax mapped to 7), each with the fp32
+ *     order t = fl(Q s_t), s_b = E4M3(fl(amax / t)), d = fl(s_t s_b),
+ *     c = code(fl(y / d));
+ *   - INT4 is kept only if its error SSE = sum fl(e_i^2), e_i =
+ *     fl(y_i - fl(c_i d)), summed in fp32 as four sequential runs of 8
+ *     followed by (P0 + P1) + (P2 + P3), is strictly smaller.
+ * Outputs: q[rows][k/2] codes (element 2j in the low nibble), s[rows][k/16]
+ * E4M3 codes, meta[rows][k/32] (bit 7 = INT4, bits 0-4 = residual
+ * position), res[rows][k/32] bf16 residual bits, and *gscale = s_t.
+ * compute_gscale != 0: s_t = fl(amax' / 2688) over the residual-free
+ * rotated tensor (1 if it is all zero) is computed and written (q serves as
+ * scratch for the partial maxima before it receives the codes); == 0:
+ * *gscale is read (finite, > 0).  k % 32 == 0; every array 16-byte aligned,
+ * gscale 4-byte aligned.  Errors as nvq_quantize.
+ */
+MXQ_API mxq_status mxq_transfp4_quantize(const void *x, mxq_dtype xdt, int64_t rows, int64_t k,
+                                 float *gscale, int compute_gscale, uint8_t *q, uint8_t *s,
+                                 uint8_t *meta, uint16_t *res, hipStream_t stream);
+
+/*
+ * TransFP4 dequantize: y_hat_i = fl(c_i * fl(s_t * E4M3(s_h))) with the
+ * codebook the block's tag selects, plus the bf16 residual at its
+ * position, then x_hat = H_32 y_hat (H is symmetric and orthonormal, so
+ * H^T = H) in the same fp32 butterfly order; written as ydt (bf16: the fp32
+ * result rounded to nearest even).  Layout as mxq_transfp4_quantize.
+ */
+MXQ_API mxq_status mxq_transfp4_dequantize(const uint8_t *q, const uint8_t *s,
+                                   const uint8_t *meta, const uint16_t *res,
+                                   const float *gscale, int64_t rows, int64_t k, void *y,
+                                   mxq_dtype ydt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

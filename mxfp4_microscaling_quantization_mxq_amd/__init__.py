@@ -34,7 +34,7 @@ STATUS = {
 API = (
     "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_quantize_fp8",
     "mxq_dequantize", "mxq_gemv_w4a16", "mxq_gemm_w4a4", "mxq_gemm_w4a4_quant", "mxq_gemm_w4a8",
-    "nvq_quantize", "nvq_dequantize", "nvq_gemm",
+    "nvq_quantize", "nvq_dequantize", "nvq_gemm", "mxq_transfp4_quantize", "mxq_transfp4_dequantize",
 )
 
 
@@ -74,6 +74,8 @@ def capi() -> ctypes.CDLL:
     lib.nvq_quantize.argtypes = [P, I, I64, I64, P, I, P, P, P]
     lib.nvq_dequantize.argtypes = [P, P, P, I64, I64, P, I, P]
     lib.nvq_gemm.argtypes = [P, P, P, I64, I64, P, I64, P, I, P]
+    lib.mxq_transfp4_quantize.argtypes = [P, I, I64, I64, P, I, P, P, P, P, P]
+    lib.mxq_transfp4_dequantize.argtypes = [P, P, P, P, P, I64, I64, P, I, P]
     for name in API[2:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -290,6 +292,50 @@ def nv_dequantize(q, s, g, dtype=None, y=None):
         y = torch.empty((rows, k), dtype=dtype, device=q.device)
     _check(capi().nvq_dequantize(_p(q), _p(s), _p(g), rows, k, _p(y), _dtype_code(y.dtype), _stream()),
            "nvq_dequantize")
+    return y
+
+
+# ------------------------------------------------------------------ TransFP4 blocks
+
+def transfp4_quantize(x, gscale=None, q=None, s=None, meta=None, res=None, g=None):
+    """TransFP4 quantize x[rows, k] -> (q[rows, k/2], s[rows, k/16] E4M3,
+    meta[rows, k/32] (bit 7 INT4 tag, bits 0-4 residual position),
+    res[rows, k/32] bf16 residuals, g[1] fp32 tensor scale).  gscale as in
+    nv_quantize."""
+    torch = _torch()
+    _need(x, "x")
+    rows, k = x.shape
+    compute = gscale is None
+    if compute:
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=x.device)
+    elif isinstance(gscale, (float, int)):
+        g = torch.tensor([float(gscale)], dtype=torch.float32, device=x.device)
+    else:
+        g = gscale
+    dev = x.device
+    q = q if q is not None else torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    s = s if s is not None else torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
+    meta = meta if meta is not None else torch.empty((rows, k // 32), dtype=torch.uint8, device=dev)
+    res = res if res is not None else torch.empty((rows, k // 32), dtype=torch.bfloat16, device=dev)
+    _check(capi().mxq_transfp4_quantize(_p(x), _dtype_code(x.dtype), rows, k, _p(g), int(compute), _p(q), _p(s),
+                                        _p(meta), _p(res), _stream()), "mxq_transfp4_quantize")
+    return q, s, meta, res, g
+
+
+def transfp4_dequantize(q, s, meta, res, g, dtype=None, y=None):
+    """x_hat[rows, k] (fp32 or bf16) from the TransFP4 arrays."""
+    torch = _torch()
+    dtype = dtype or torch.float32
+    _need(q, "q", torch.uint8)
+    _need(s, "s", torch.uint8)
+    _need(meta, "meta", torch.uint8)
+    _need(res, "res", torch.bfloat16)
+    rows, k = q.shape[0], q.shape[1] * 2
+    if y is None:
+        y = torch.empty((rows, k), dtype=dtype, device=q.device)
+    _check(capi().mxq_transfp4_dequantize(_p(q), _p(s), _p(meta), _p(res), _p(g), rows, k, _p(y),
+                                          _dtype_code(y.dtype), _stream()), "mxq_transfp4_dequantize")
     return y
 
 

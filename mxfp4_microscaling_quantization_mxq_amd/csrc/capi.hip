@@ -234,4 +234,35 @@ mxq_status nvq_dequantize(const uint8_t* q, const uint8_t* s, const float* gscal
   return launched(mxq::launch_nv_dequantize(q, s, gscale, rows, k, y, ydt == MXQ_BF16, stream));
 }
 
+mxq_status mxq_transfp4_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, float* gscale,
+                                 int compute_gscale, uint8_t* q, uint8_t* s, uint8_t* meta, uint16_t* res,
+                                 hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
+  if (!x || !q || !s || !meta || !res || !gscale) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(meta) || !aligned16(res))
+    return MXQ_ERROR_MISALIGNED;
+  if ((uintptr_t)gscale & 3u) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_tf4_quantize(x, xdt == MXQ_BF16, rows, k, gscale, compute_gscale != 0, q, s, meta,
+                                           res, stream));
+}
+
+mxq_status mxq_transfp4_dequantize(const uint8_t* q, const uint8_t* s, const uint8_t* meta, const uint16_t* res,
+                                   const float* gscale, int64_t rows, int64_t k, void* y, mxq_dtype ydt,
+                                   hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
+  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
+  if (!q || !s || !meta || !res || !gscale || !y) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(meta) || !aligned16(res) || !aligned16(y))
+    return MXQ_ERROR_MISALIGNED;
+  if ((uintptr_t)gscale & 3u) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_tf4_dequantize(q, s, meta, res, gscale, rows, k, y, ydt == MXQ_BF16, stream));
+}
+
 }  // extern "C"

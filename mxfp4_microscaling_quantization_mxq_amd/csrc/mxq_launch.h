@@ -25,6 +25,12 @@ hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows
                                 bool bf16, hipStream_t st);
 hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,
                               bool compute_gscale, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_tf4_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,
+                               bool compute_gscale, uint8_t* q, uint8_t* s, uint8_t* meta, uint16_t* res,
+                               hipStream_t st);
+hipError_t launch_tf4_dequantize(const uint8_t* q, const uint8_t* s, const uint8_t* meta, const uint16_t* res,
+                                 const float* gscale, int64_t rows, int64_t k, void* y, bool bf16_out,
+                                 hipStream_t st);
 hipError_t launch_nv_dequantize(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows,
                                 int64_t k, void* y, bool bf16, hipStream_t st);
 

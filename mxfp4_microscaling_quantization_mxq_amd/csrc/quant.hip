@@ -205,16 +205,9 @@ __device__ __forceinline__ void butterfly_across_lanes(float (&v)[8], int lane) 
   }
 }
 
-template <bool kBf16In, int HK>
-__global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __restrict__ x, unsigned* __restrict__ q,
-                                                              uint8_t* __restrict__ s, int64_t nlanes) {
-  static_assert(HK == 16 || HK == 32 || HK == 64 || HK == 128, "rotation size");
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // nlanes is a multiple of HK / 8 and of 4, and blocks hold 256 lanes:
-  // rotation groups and MXFP4 quads are whole or absent
-  if (t >= nlanes) return;
-  const int lane = threadIdx.x & 63;
-  float v[8];
+// One lane's 8 consecutive elements (lane t of the tensor) as fp32.
+template <bool kBf16In>
+__device__ __forceinline__ void load8(const u32x4* __restrict__ x, int64_t t, float (&v)[8]) {
   if (kBf16In) {
     const u32x4 w = __builtin_nontemporal_load(&x[t]);
     const unsigned ww[4] = {w.x, w.y, w.z, w.w};
@@ -230,6 +223,12 @@ __global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __res
 #pragma unroll
     for (int i = 0; i < 8; i++) v[i] = __uint_as_float(ww[i]);
   }
+}
+
+// H_HK applied to the HK-block that this lane's 8 values belong to (HK / 8
+// consecutive lanes), in the fixed order described above.
+template <int HK>
+__device__ __forceinline__ void rotate8(float (&v)[8], int lane) {
   // stages h = 1, 2, 4 inside the lane
 #pragma unroll
   for (int h = 1; h < 8; h *= 2)
@@ -248,6 +247,20 @@ __global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __res
   const float c = hadamard_norm<HK>();
 #pragma unroll
   for (int i = 0; i < 8; i++) v[i] = v[i] * c;
+}
+
+template <bool kBf16In, int HK>
+__global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __restrict__ x, unsigned* __restrict__ q,
+                                                              uint8_t* __restrict__ s, int64_t nlanes) {
+  static_assert(HK == 16 || HK == 32 || HK == 64 || HK == 128, "rotation size");
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // nlanes is a multiple of HK / 8 and of 4, and blocks hold 256 lanes:
+  // rotation groups and MXFP4 quads are whole or absent
+  if (t >= nlanes) return;
+  const int lane = threadIdx.x & 63;
+  float v[8];
+  load8<kBf16In>(x, t, v);
+  rotate8<HK>(v, lane);
   // MXFP4 of the rotated block (as k_mx_quantize_f32)
   unsigned m = 0;
 #pragma unroll
@@ -441,6 +454,266 @@ __global__ __launch_bounds__(256) void k_nv_dequantize(const unsigned* __restric
   }
 }
 
+// ---------------------------------------------------------------- TransFP4 blocks
+
+// TransFP4 [TransFP4 page sec. 2.3 eq. (3): x_hat = H^T Q_f(Hx - P_r Hx) +
+// H^T P_r Hx; sec. 3.1: a 32-point Hadamard, at most one residual per 32
+// values, and per block the NVFP4 or the INT4 candidate by block error].
+// Per 32-block (four lanes):
+//   * y = H_32 x as rotate8<32> (the rotated-MXFP4 order);
+//   * the residual: the largest |y_i| (first position on ties), stored as
+//     bf16 (nearest even) and set to +0 in the block Q_f sees;
+//   * two candidates under E4M3 scales per 16 and the fp32 tensor scale
+//     s_t = amax' / 2688 of the residual-free rotated tensor, with the
+//     NVFP4 order of operations: t = fl(Q s_t), s_b = E4M3(fl(amax_16 / t)),
+//     d = fl(s_t s_b), v = fl(y / d) correctly rounded -- the E2M1 codebook
+//     with Q = 6, and INT4 (sign and magnitude 0..7, nearest even,
+//     saturating) with Q = 7;
+//   * block error SSE = sum fl(e^2), e = fl(y - fl(c d)): each lane sums its
+//     8 terms in order, then the quad adds (P0 + P1) + (P2 + P3); INT4 is
+//     kept only if its SSE is strictly smaller.
+// Storage per block: 16 code bytes, two E4M3 scales, a meta byte (bit 7:
+// INT4, bits 0-4: residual position) and the bf16 residual.
+
+// Residual of a rotated 32-block: the block position of the largest |v|
+// (first on ties) is returned to every lane of the quad; the lane that holds
+// it takes the value into rv and zeroes it.
+__device__ __forceinline__ int tf4_split(float (&v)[8], int lane, float& rv) {
+  const int ql = lane & 3;
+  unsigned best = __float_as_uint(v[0]) & 0x7FFFFFFFu;
+  unsigned at = 8u * ql;
+#pragma unroll
+  for (int i = 1; i < 8; i++) {
+    const unsigned a = __float_as_uint(v[i]) & 0x7FFFFFFFu;  // |v| orders like its bits
+    if (a > best) {
+      best = a;
+      at = 8u * ql + i;
+    }
+  }
+  {
+    const unsigned ob = dpp_quad_xor1(best), oa = dpp_quad_xor1(at);
+    const bool take = ob > best || (ob == best && oa < at);
+    best = take ? ob : best;
+    at = take ? oa : at;
+  }
+  {
+    const unsigned ob = dpp_quad_xor2(best), oa = dpp_quad_xor2(at);
+    const bool take = ob > best || (ob == best && oa < at);
+    best = take ? ob : best;
+    at = take ? oa : at;
+  }
+  const bool own = (int)(at >> 3) == ql;
+  rv = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const bool hit = own && (int)(at & 7u) == i;
+    rv = hit ? v[i] : rv;
+    v[i] = hit ? 0.0f : v[i];
+  }
+  return (int)at;
+}
+
+__device__ __forceinline__ float quad_xor1_f(float v) { return __uint_as_float(dpp_quad_xor1(__float_as_uint(v))); }
+__device__ __forceinline__ float quad_xor2_f(float v) { return __uint_as_float(dpp_quad_xor2(__float_as_uint(v))); }
+
+// One candidate for this lane's 8 residual-free values (16-block amax known):
+// packed codes, the E4M3 scale code and the block SSE (same on all 4 lanes).
+template <bool kInt4>
+__device__ __forceinline__ void tf4_candidate(const float (&v)[8], float amax, float st, unsigned& codes,
+                                              unsigned& sb, float& sse) {
+  sb = e4m3_encode_nonneg(__fdiv_rn(amax, (kInt4 ? 7.0f : 6.0f) * st));
+  const float sbv = e4m3_value(sb);
+  float e[8];
+  unsigned out = 0;
+  if (sbv == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      out |= (__float_as_uint(v[i]) >> 31) << (3 + 4 * i);
+      e[i] = v[i];
+    }
+  } else {
+    const float d = st * sbv;
+    float qv[8];
+    if (d >= 0x1p-100f && amax <= d * 0x1p100f) {
+      const float y = __fdiv_rn(1.0f, d);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const unsigned xb = __float_as_uint(v[i]);
+        const float aq = div_by_block_scale(__uint_as_float(xb & 0x7FFFFFFFu), d, y);
+        qv[i] = __uint_as_float(__float_as_uint(aq) | (xb & 0x80000000u));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) qv[i] = __fdiv_rn(v[i], d);
+    }
+    float cv[8];
+    if constexpr (kInt4) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float mag = fminf(__builtin_rintf(fabsf(qv[i])), 7.0f);  // nearest, ties to even
+        const unsigned sg = __float_as_uint(qv[i]) >> 31;
+        out |= (((unsigned)mag) | (sg << 3)) << (4 * i);
+        cv[i] = sg ? -mag : mag;
+      }
+    } else {
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, qv[0], qv[1], 1.0f, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, qv[2], qv[3], 1.0f, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, qv[4], qv[5], 1.0f, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, qv[6], qv[7], 1.0f, 3);
+      const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(out, 1.0f, 0);
+      const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(out, 1.0f, 1);
+      const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(out, 1.0f, 2);
+      const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(out, 1.0f, 3);
+      cv[0] = p0[0]; cv[1] = p0[1]; cv[2] = p1[0]; cv[3] = p1[1];
+      cv[4] = p2[0]; cv[5] = p2[1]; cv[6] = p3[0]; cv[7] = p3[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float dq = cv[i] * d;
+      e[i] = v[i] - dq;
+    }
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float sq = e[i] * e[i];
+    acc = acc + sq;
+  }
+  acc = acc + quad_xor1_f(acc);  // lanes 0,1: P0 + P1; lanes 2,3: P2 + P3
+  acc = acc + quad_xor2_f(acc);  // (P0 + P1) + (P2 + P3) on every lane
+  codes = out;
+  sse = acc;
+}
+
+// Pass 1: per block of this grid, the largest |y'| (residual-free rotated
+// values) of its grid-stride share, as fp32 bits, into part[block]; then
+// k_nv_scale folds the partials into s_t = amax' / 2688.
+constexpr int kTf4U = 4;  // lane slots per thread per step (loads in flight)
+
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_tf4_amax(const u32x4* __restrict__ x, int64_t nlanes,
+                                                  unsigned* __restrict__ part) {
+  __shared__ unsigned wmax[4];
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  unsigned m = 0;
+  // slot u of a step is lane base + u * stride; stride, base - threadIdx.x
+  // and nlanes are multiples of 4, so each quad (one 32-block) is whole
+  for (int64_t base = (int64_t)blockIdx.x * 256 + threadIdx.x; base - threadIdx.x < nlanes;
+       base += kTf4U * stride) {
+    float v[kTf4U][8];
+#pragma unroll
+    for (int u = 0; u < kTf4U; u++) {
+      const int64_t t = base + u * stride;
+      if (t < nlanes) {
+        load8<kBf16In>(x, t, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTf4U; u++) {
+      rotate8<32>(v[u], lane);
+      float rv;
+      tf4_split(v[u], lane, rv);
+#pragma unroll
+      for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+}
+
+// Pass 2: one lane = 8 elements, a quad = one 32-block, a lane pair = one
+// 16-element scale block.
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_tf4_quantize(const u32x4* __restrict__ x, const float* __restrict__ g,
+                                                      unsigned* __restrict__ q, uint8_t* __restrict__ s,
+                                                      uint8_t* __restrict__ meta, uint16_t* __restrict__ res,
+                                                      int64_t nlanes) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;  // nlanes % 4 == 0: quads stay whole
+  const int lane = threadIdx.x & 63;
+  const float st = *g;
+  float v[8];
+  load8<kBf16In>(x, t, v);
+  rotate8<32>(v, lane);
+  float rv;
+  const int at = tf4_split(v, lane, rv);
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  m = max(m, dpp_quad_xor1(m));  // the 16-element half
+  const float amax = __uint_as_float(m);
+  unsigned cn, ci, sn, si;
+  float en, ei;
+  tf4_candidate<false>(v, amax, st, cn, sn, en);
+  tf4_candidate<true>(v, amax, st, ci, si, ei);
+  const bool int4 = ei < en;
+  q[t] = int4 ? ci : cn;
+  if ((t & 1) == 0) s[t >> 1] = (uint8_t)(int4 ? si : sn);
+  if ((t & 3) == 0) meta[t >> 2] = (uint8_t)((int4 ? 0x80u : 0u) | (unsigned)at);
+  if ((at >> 3) == (lane & 3)) res[t >> 2] = f32_to_bf16_rne(rv);
+}
+
+// Dequantize: y_hat = fl(c * fl(s_t * E4M3(s_b))) with the codebook the tag
+// selects, the residual added at its position, then x_hat = H^T y_hat = H
+// y_hat (H_32 is symmetric and orthonormal) in the same butterfly order.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void k_tf4_dequantize(const unsigned* __restrict__ q,
+                                                        const uint8_t* __restrict__ s,
+                                                        const uint8_t* __restrict__ meta,
+                                                        const uint16_t* __restrict__ res,
+                                                        const float* __restrict__ g, void* __restrict__ y,
+                                                        int64_t nlanes) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nlanes) return;
+  const int lane = threadIdx.x & 63;
+  const unsigned c = q[t];
+  const float d = *g * e4m3_value(s[t >> 1]);
+  const unsigned mb = meta[t >> 2];
+  const int at = (int)(mb & 31u);
+  float v[8];
+  if (mb & 0x80u) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const unsigned ci = (c >> (4 * i)) & 15u;
+      const float mag = (float)(ci & 7u);
+      v[i] = (ci & 8u) ? -mag : mag;
+    }
+  } else {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = v[i] * d;
+  if ((at >> 3) == (lane & 3)) {
+    const float rv = __uint_as_float((unsigned)res[t >> 2] << 16);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if ((at & 7) == i) v[i] = v[i] + rv;
+  }
+  rotate8<32>(v, lane);
+  if (kBf16Out) {
+    u32x4 o;
+    o.x = f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+    o.y = f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+    o.z = f32_to_bf16_rne(v[4]) | ((unsigned)f32_to_bf16_rne(v[5]) << 16);
+    o.w = f32_to_bf16_rne(v[6]) | ((unsigned)f32_to_bf16_rne(v[7]) << 16);
+    ((u32x4*)y)[t] = o;
+  } else {
+    ((f32x4*)y)[2 * t] = (f32x4){v[0], v[1], v[2], v[3]};
+    ((f32x4*)y)[2 * t + 1] = (f32x4){v[4], v[5], v[6], v[7]};
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
@@ -539,6 +812,42 @@ hipError_t launch_nv_dequantize(const uint8_t* q, const uint8_t* s, const float*
   else
     hipLaunchKernelGGL(k_nv_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
                        (const unsigned*)q, s, gscale, y, nlanes);
+  return hipGetLastError();
+}
+
+hipError_t launch_tf4_quantize(const void* x, bool bf16, int64_t rows, int64_t k, float* gscale,
+                               bool compute_gscale, uint8_t* q, uint8_t* s, uint8_t* meta, uint16_t* res,
+                               hipStream_t st) {
+  const int64_t nlanes = rows * k / 8;
+  if (compute_gscale) {
+    // partials go to the code buffer (4 * nlanes bytes >= 4 * np)
+    const int np = (int)std::max<int64_t>(1, std::min<int64_t>(grid_for(nlanes, 256 * kTf4U), 2048));
+    unsigned* part = (unsigned*)q;
+    if (bf16)
+      hipLaunchKernelGGL(k_tf4_amax<true>, dim3(np), dim3(256), 0, st, (const u32x4*)x, nlanes, part);
+    else
+      hipLaunchKernelGGL(k_tf4_amax<false>, dim3(np), dim3(256), 0, st, (const u32x4*)x, nlanes, part);
+    hipLaunchKernelGGL(k_nv_scale, dim3(1), dim3(256), 0, st, (const unsigned*)part, np, gscale);
+  }
+  if (bf16)
+    hipLaunchKernelGGL(k_tf4_quantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (const float*)gscale, (unsigned*)q, s, meta, res, nlanes);
+  else
+    hipLaunchKernelGGL(k_tf4_quantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+                       (const float*)gscale, (unsigned*)q, s, meta, res, nlanes);
+  return hipGetLastError();
+}
+
+hipError_t launch_tf4_dequantize(const uint8_t* q, const uint8_t* s, const uint8_t* meta, const uint16_t* res,
+                                 const float* gscale, int64_t rows, int64_t k, void* y, bool bf16_out,
+                                 hipStream_t st) {
+  const int64_t nlanes = rows * k / 8;
+  if (bf16_out)
+    hipLaunchKernelGGL(k_tf4_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const unsigned*)q, s,
+                       meta, res, gscale, y, nlanes);
+  else
+    hipLaunchKernelGGL(k_tf4_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const unsigned*)q,
+                       s, meta, res, gscale, y, nlanes);
   return hipGetLastError();
 }
 

@@ -148,6 +148,22 @@ def test_nv_quantize_validation(lib):
     assert d(A16, A16b, A16d, 4, 8, A16c, 1, NULL) == INVALID
 
 
+def test_transfp4_validation(lib):
+    q = lib.mxq_transfp4_quantize
+    assert q(A16, 1, 4, 48, A16b, 1, A16c, A16d, A16, A16b, NULL) == INVALID  # k % 32
+    assert q(A16, 1, 4, 64, A16b, 1, A16c, A16d, NULL, A16b, NULL) == INVALID  # meta missing
+    assert q(A16, 1, 4, 64, A16b, 1, A16c, A16d, A16, NULL, NULL) == INVALID  # res missing
+    assert q(A16, 1, 4, 64, A16b, 1, A16c, A16d, MIS, A16b, NULL) == MISALIGNED
+    assert q(A16, 1, 4, 64, ctypes.c_void_p(0x50001), 1, A16c, A16d, A16, A16b, NULL) == MISALIGNED
+    assert q(A16, 7, 4, 64, A16b, 1, A16c, A16d, A16, A16b, NULL) == INVALID  # dtype
+    assert q(NULL, 1, 0, 64, NULL, 1, NULL, NULL, NULL, NULL, NULL) == SUCCESS
+    d = lib.mxq_transfp4_dequantize
+    assert d(A16, A16b, A16c, A16d, NULL, 4, 64, A16, 0, NULL) == INVALID  # gscale missing
+    assert d(A16, A16b, A16c, A16d, A16b, 4, 40, A16, 0, NULL) == INVALID  # k % 32
+    assert d(A16, A16b, A16c, MIS, A16b, 4, 64, A16, 0, NULL) == MISALIGNED
+    assert d(NULL, NULL, NULL, NULL, NULL, 0, 64, NULL, 0, NULL) == SUCCESS
+
+
 def test_no_device_reports_not_supported(lib):
     """Valid arguments on a machine without a GPU: NOT_SUPPORTED, no launch."""
     import torch
@@ -158,6 +174,7 @@ def test_no_device_reports_not_supported(lib):
     assert lib.mxq_quantize_hadamard(A16, 1, 4, 32, 32, A16b, A16c, NULL) == NOT_SUPPORTED
     assert lib.mxq_gemm_w4a4(A16, A16b, A16c, A16d, 4, 4, 32, A16, 1, NULL) == NOT_SUPPORTED
     assert lib.nvq_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, NULL) == NOT_SUPPORTED
+    assert lib.mxq_transfp4_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, A16, A16b, NULL) == NOT_SUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

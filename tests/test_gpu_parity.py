@@ -323,6 +323,74 @@ def test_mx_quantize_hadamard_dynamic_full_size():
     assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
 
 
+# ------------------------------------------------------------------ TransFP4 blocks
+
+def assert_tf4(x_np, what, gscale=None):
+    """Codes, E4M3 scales, meta bytes, bf16 residuals and the tensor scale
+    bit-exact against the oracle; then the fp32 dequantization bit-exact and
+    the bf16 one equal to the oracle's fp32 rounded to nearest even."""
+    q, s, meta, res, g = mxq.transfp4_quantize(dev(x_np), gscale)
+    qo, so, mo, ro, go = oracle.tf4_quantize(x_np, gscale)
+    gg = float(host(g)[0])
+    assert np.float32(gg) == np.float32(go), f"{what}: s_t {gg!r} vs {go!r}"
+    for nm, a, b in (("meta", host(meta), mo), ("res", host(res), ro), ("scale", host(s), so), ("code", host(q), qo)):
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)[:5]
+            raise AssertionError(f"{what}: {nm} mismatch at {bad.tolist()}: gpu {[int(a[tuple(i)]) for i in bad]} "
+                                 f"oracle {[int(b[tuple(i)]) for i in bad]}")
+    want = oracle.tf4_dequantize(qo, so, mo, ro, go)
+    y32 = host(mxq.transfp4_dequantize(q, s, meta, res, g, torch.float32))
+    if not np.array_equal(y32.view(np.uint32), want.view(np.uint32)):
+        bad = np.argwhere(y32.view(np.uint32) != want.view(np.uint32))[:5]
+        raise AssertionError(f"{what}: dequant mismatch at {bad.tolist()}")
+    y16 = host(mxq.transfp4_dequantize(q, s, meta, res, g, torch.bfloat16))
+    assert np.array_equal(y16, synth.f32_to_bf16_bits(want)), f"{what}: bf16 dequant"
+    return mo
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 64), (37, 384), (300, 2048)])
+def test_transfp4_ragged(rows, k):
+    """Ragged shapes, bf16 and fp32 inputs with per-row magnitude spreads,
+    the tensor scale computed on the device and given by the caller."""
+    for x_np, nm in [(laplace_bf16(rows * 5 + k, rows, k), "bf16"), (laplace_f32(rows + 7 * k, rows, k), "fp32")]:
+        mo = assert_tf4(x_np, f"transfp4 {rows}x{k} {nm}")
+        assert_tf4(x_np, f"transfp4 {rows}x{k} {nm} given s_t", gscale=0.0371)
+        if rows * k >= 4096:
+            assert (mo & 0x80).any() and (~mo & 0x80).any(), "both codebooks should occur"
+
+
+def test_transfp4_edge_values():
+    """Argmax ties (a one-hot input rotates to 32 equal magnitudes), zero and
+    signed-zero blocks, a lone outlier, huge and tiny values, blocks that are
+    exact on either grid before rotation."""
+    x = np.zeros((10, 256), dtype=np.float32)
+    x[1, :] = -0.0
+    x[2, 5] = 1e30
+    x[3, ::7] = -3.5e-30
+    x[4, :] = np.exp2(np.linspace(-40, 40, 256)).astype(np.float32)
+    x[5, 100] = -7.0
+    x[6, :128] = 1e36
+    x[7, :] = np.linspace(-6, 6, 256, dtype=np.float32)
+    x[8, ::32] = 1.0  # one-hot per block: every rotated value has the same magnitude
+    x[9, :] = np.tile(np.arange(-16, 16, dtype=np.float32), 8)
+    mo = assert_tf4(x, "transfp4 edges")
+    assert np.all(mo[8] & 31 == 0)
+    assert_tf4(np.zeros((4, 64), dtype=np.float32), "transfp4 all-zero tensor")
+
+
+def test_transfp4_table5_tensor_and_full_size():
+    """The 131,072-element Table 5 activation tensor (NMSE reported next to
+    the oracle's), and the 16384 x 8192 activation tensor, bit-exact."""
+    x = synth.table4_activations().reshape(128, 1024)
+    assert_tf4(x, "transfp4 table5 tensor")
+    q, s, meta, res, g = mxq.transfp4_quantize(dev(x))
+    xh = host(mxq.transfp4_dequantize(q, s, meta, res, g, torch.float32)).astype(np.float64)
+    nm, c = oracle.metrics(x.astype(np.float64), xh)
+    say(f"TransFP4 on the Table 5 activation tensor: NMSE {nm:.5f}, cosine {c:.5f}, "
+        f"INT4 blocks {float((host(meta) & 0x80).mean()):.3f}")
+    assert_tf4(dynamic_quantize_input(), "transfp4 16384x8192")
+
+
 def test_rotated_operands_keep_the_product():
     """H is orthonormal, so (X H)(W H)^T = X W^T: the W4A4 GEMM of rotated
     MXFP4 operands approximates the unquantized product (and more closely than
