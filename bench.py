@@ -6,7 +6,9 @@ One step runs every row of the hot path once, on seeded synthetic inputs
 already resident in HBM:
   tiny   MXFP4 quantize (fp32 256x512) + dequantize + W4A16 GEMV (m=1)
   quant  dynamic MXFP4 quantize of bf16 activations 16384x8192, plain and
-         with the 32-point block Hadamard rotation fused ahead of it
+         with the 32-point block Hadamard rotation fused ahead of it; the
+         TransFP4 block quantize (rotation, bf16 residual, NVFP4/INT4 choice)
+         of the same tensor and its dequantization
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
          (bf16 output, and MXFP4 output quantized in the epilogue); MXFP8
@@ -144,6 +146,23 @@ def main():
         # rotated MXFP4 (32-point block Hadamard fused ahead of the quantizer)
         ops.append(("quantize_hadamard32_16384x8192_bf16",
                     rotating(sets, lambda x, q, s: mxq.quantize_hadamard(x, 32, q, s)), quant_bytes(16384, 8192), 0))
+        # TransFP4 blocks: tensor-scale pass + quantize pass (x read twice),
+        # then the dequantization back to bf16
+        ntf = 16384 * 8192
+        tsets = [(x, torch.empty((16384, 4096), dtype=u8, device=dev), torch.empty((16384, 512), dtype=u8, device=dev),
+                  torch.empty((16384, 256), dtype=u8, device=dev), torch.empty((16384, 256), dtype=bf16, device=dev),
+                  torch.empty(1, dtype=torch.float32, device=dev)) for x, _, _ in sets]
+        tf4_bytes = ntf // 2 + ntf // 16 + ntf // 32 + ntf // 16  # codes, E4M3, meta, bf16 residual
+        ops.append(("transfp4_quantize_16384x8192_bf16",
+                    rotating(tsets, lambda x, q, s, m, r, g: mxq.transfp4_quantize(x, None, q, s, m, r, g)),
+                    2 * 2 * ntf + tf4_bytes, 0))
+        ydq = [torch.empty((16384, 8192), dtype=bf16, device=dev) for _ in tsets]
+        for (x, q, s_, m, r, g) in tsets:
+            mxq.transfp4_quantize(x, None, q, s_, m, r, g)
+        ops.append(("transfp4_dequantize_16384x8192_bf16",
+                    rotating([(q, s_, m, r, g, y) for (x, q, s_, m, r, g), y in zip(tsets, ydq)],
+                             lambda q, s_, m, r, g, y: mxq.transfp4_dequantize(q, s_, m, r, g, y=y)),
+                    tf4_bytes + 2 * ntf, 0))
     if "gemv" in parts:
         n2, k2 = 28672, 8192
         w2, _ = synth.decode_gemv(1)
