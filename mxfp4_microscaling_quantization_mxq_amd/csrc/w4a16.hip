@@ -464,13 +464,24 @@ __device__ __forceinline__ GSlot& g_slot() {
   return slot;
 }
 
-template <bool kNv, bool kBf16Out>
-__global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+// NWV waves per block: 4 (2 x 2 wave tiles of 128 x 128, one wave per SIMD)
+// or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's MFMAs cover the
+// other's fragment reads, expansion and waits).
+template <bool kNv, bool kBf16Out, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
                                                        const float* __restrict__ gscale, int64_t n, int64_t k,
                                                        const uint16_t* __restrict__ x, int64_t m,
                                                        void* __restrict__ y) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
+  constexpr int WNC = NWV / 2;         // wave columns
+  constexpr int WCOLS = kGBN / WNC;    // weight rows (output columns) per wave
+  constexpr int JB = WCOLS / 32;       // weight fragments per wave
+  constexpr int RPW = kGBM / NWV;      // rows of x and of W each wave copies
+  constexpr int CJX = RPW / 8;         // x copies per wave per stage (8 rows of 128 B each)
+  constexpr int CJW = RPW / 32;        // weight copies per wave per stage (32 rows of 32 B each)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WNC, wn = wave % WNC;
   const int half = lane >> 5, r32 = lane & 31;
 
   const int64_t tm_n = (m + kGBM - 1) / kGBM, tn_n = (n + kGBN - 1) / kGBN;
@@ -487,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
   const int nstages = (int)(k / 64);
 
-  // 10 DMA instructions per wave per stage: 8 for x, 2 for weight codes
+  // CJX + CJW DMA instructions per wave per stage (10 with 4 waves, 5 with 8)
   // stage s into ring slot b (near the end the stage index is clamped to the
   // last stage so every step issues the same number of loads; the copy lands
   // in the free slot and is never read)
@@ -495,16 +506,17 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   // the whole k loop, the stage moves the uniform offset only
   const __amdgpu_buffer_rsrc_t rx = make_rsrc((const uint8_t*)x + m0 * kx, (unsigned)(rows_x * kx));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * kq, (unsigned)(rows_w * kq));
-  unsigned offx[8], offw[2];
+  unsigned offx[CJX], offw[CJW];
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int row = 64 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < CJX; j++) {
+    // (row >> 1) & 7 == (4 j + lane / 16) & 7: RPW * wave / 2 is a multiple of 8
+    const int row = RPW * wave + 8 * j + (lane >> 3);
     const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
     offx[j] = (unsigned)min(row, rows_x - 1) * (unsigned)kx + cu16;
   }
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int row = 64 * wave + 32 * j + (lane >> 1);
+  for (int j = 0; j < CJW; j++) {
+    const int row = RPW * wave + 32 * j + (lane >> 1);
     const unsigned cu16 = (unsigned)(((lane & 1) ^ ((row >> 3) & 1)) << 4);
     offw[j] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + cu16;
   }
@@ -512,16 +524,16 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
     uint8_t* xb = g_slot<decltype(slot_tag)::value>().x;
     uint8_t* wb = g_slot<decltype(slot_tag)::value>().w;
 #pragma unroll
-    for (int j = 0; j < 8; j++) bdma16(rx, offx[j], (unsigned)s * 128u, xb + (64 * wave + 8 * j) * 128);
+    for (int j = 0; j < CJX; j++) bdma16(rx, offx[j], (unsigned)s * 128u, xb + (RPW * wave + 8 * j) * 128);
 #pragma unroll
-    for (int j = 0; j < 2; j++) bdma16(rw, offw[j], (unsigned)s * 32u, wb + (64 * wave + 32 * j) * 32);
+    for (int j = 0; j < CJW; j++) bdma16(rw, offw[j], (unsigned)s * 32u, wb + (RPW * wave + 32 * j) * 32);
   };
   // this lane's scale byte(s) for its four weight rows at stage s (global,
   // L2-resident): MXFP4 block 2s + half; NVFP4 blocks 4s + 2 half + {0, 1}
-  auto load_scales = [&](int s, unsigned sc[4]) {
+  auto load_scales = [&](int s, unsigned sc[JB]) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t row = min(n0 + wn * 128 + j * 32 + r32, n - 1);
+    for (int j = 0; j < JB; j++) {
+      const int64_t row = min(n0 + wn * WCOLS + j * 32 + r32, n - 1);
       if (kNv) {
         const uint8_t* p = ws + row * ks + 4 * (int64_t)s + 2 * half;
         sc[j] = p[0] | ((unsigned)p[1] << 8);
@@ -531,22 +543,22 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (f32x16){};
+    for (int j = 0; j < JB; j++) acc[i][j] = (f32x16){};
 
   const int swz = (r32 >> 1) & 7;
   const int laneX = (wm * 128 + r32) * 128;
-  const int laneW = (wn * 128 + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
+  const int laneW = (wn * WCOLS + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
 
   // weight operands of k step kk from the stage's code chunks: MXFP4 with
   // the scaled convert (exact bf16), NVFP4 as E4M3 * E2M1 in fp32 (exact,
   // at most 6 significant bits) rounded to bf16 (exact)
-  auto dequant = [&](const u32x4 wc[4], int kk, const unsigned sc[4], bf16x8 wf[4]) {
+  auto dequant = [&](const u32x4 wc[JB], int kk, const unsigned sc[JB], bf16x8 wf[JB]) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < JB; j++) {
       const unsigned d = kk == 0 ? wc[j].x : kk == 1 ? wc[j].y : kk == 2 ? wc[j].z : wc[j].w;
       if (!kNv) {
         const float scale = e8m0_as_scale(sc[j] & 0xFFu);
@@ -574,13 +586,13 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   // Software pipeline inside a stage (fixed by scheduling fences): the
   // activation fragments of step kk+1 are read and the weight operands of
   // step kk+1 are expanded while the 16 MFMAs of step kk run.
-  auto compute = [&](auto slot_tag, const unsigned sc[4]) {
+  auto compute = [&](auto slot_tag, const unsigned sc[JB]) {
     const uint8_t* xb = g_slot<decltype(slot_tag)::value>().x;
     const uint8_t* wb = g_slot<decltype(slot_tag)::value>().w;
-    u32x4 wc[4];
+    u32x4 wc[JB];
 #pragma unroll
-    for (int j = 0; j < 4; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
-    bf16x8 xf[2][4], wf[2][4];
+    for (int j = 0; j < JB; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
+    bf16x8 xf[2][4], wf[2][JB];
     read_x(xb, 0, xf[0]);
     dequant(wc, 0, sc, wf[0]);
 #pragma unroll
@@ -592,12 +604,12 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < JB; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[c][j], xf[c][i], acc[i][j], 0, 0, 0);
       // reads first, then each MFMA followed by a share of the expansion
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int g = 0; g < 16; g++) {
+      for (int g = 0; g < 4 * JB; g++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kNv ? 4 : 2, 0);
       }
@@ -606,11 +618,11 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   };
 
   // one stage s in ring slot B: fetch the next stage's scales, wait for
-  // stage s (stage s+1's 10 copies and the 4 scale loads may stay in
-  // flight), meet, refill the slot of stage s-1 with stage s+2 (clamped to
+  // stage s (stage s+1's CJX + CJW copies and the JB scale loads may stay
+  // in flight; NVFP4's two-byte scale loads only make the wait longer), meet, refill the slot of stage s-1 with stage s+2 (clamped to
   // the last stage near the end: the copy lands in a free slot), multiply.
   // Slot indices are compile-time constants (the loop is unrolled by 3).
-  unsigned sc_cur[4], sc_nxt[4];
+  unsigned sc_cur[JB], sc_nxt[JB];
   // (scheduling fences keep the scale loads and the copies where they are
   // written: the scheduler would sink them next to their first use)
   auto step = [&](auto slot_tag, int s) {
@@ -618,14 +630,14 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
     __builtin_amdgcn_sched_barrier(0);
     load_scales(min(s + 1, nstages - 1), sc_nxt);
     __builtin_amdgcn_sched_barrier(0);
-    gwait_vmcnt<10 + 4>();
+    gwait_vmcnt<CJX + CJW + JB>();
     __builtin_amdgcn_s_barrier();  // no fence: the prefetched stages stay in flight
     __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, (B + kGRing - 1) % kGRing>{}, min(s + kGRing - 1, nstages - 1));
     __builtin_amdgcn_sched_barrier(0);
     compute(slot_tag, sc_cur);
 #pragma unroll
-    for (int j = 0; j < 4; j++) sc_cur[j] = sc_nxt[j];
+    for (int j = 0; j < JB; j++) sc_cur[j] = sc_nxt[j];
   };
   static_assert(kGRing == 3, "the stage loop is unrolled by the ring depth");
   // prologue: stages 0, 1 in flight
@@ -649,10 +661,10 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
     const int64_t row = m0 + wm * 128 + i * 32 + r32;
     if (row >= m) continue;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < JB; j++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int64_t col = n0 + wn * 128 + j * 32 + q * 8 + 4 * half;
+        const int64_t col = n0 + wn * WCOLS + j * 32 + q * 8 + 4 * half;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) v[e] = kNv ? acc[i][j][4 * q + e] * st : acc[i][j][4 * q + e];
@@ -677,16 +689,21 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint8_t* __restrict
   }
 }
 
+#ifndef MXQ_W4A16_GEMM_WAVES
+#define MXQ_W4A16_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = MXQ_W4A16_GEMM_WAVES;
+
 template <bool kNv>
 static void launch_gemm(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                         const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   const unsigned tiles = (unsigned)(((m + kGBM - 1) / kGBM) * ((n + kGBN - 1) / kGBN));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_gemm<kNv, true>), dim3(tiles), dim3(256), 0, st, wq, ws, gscale, n, k,
-                       (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, true, kGemmWaves>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq, ws,
+                       gscale, n, k, (const uint16_t*)x, m, y);
   else
-    hipLaunchKernelGGL((k_w4a16_gemm<kNv, false>), dim3(tiles), dim3(256), 0, st, wq, ws, gscale, n, k,
-                       (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, false, kGemmWaves>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq, ws,
+                       gscale, n, k, (const uint16_t*)x, m, y);
 }
 
 template <bool kNv, int R, int U, int W>
