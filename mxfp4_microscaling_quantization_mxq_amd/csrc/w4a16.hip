@@ -656,6 +656,45 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
   gwait_vmcnt<0>();
 
   const float st = kNv ? *gscale : 1.0f;
+  if constexpr (kBf16Out) {
+    // lane (r32, half) holds, for each q, output columns 8q + 4 half + 0..3
+    // of its row; lanes l and l ^ 32 swap halves so that each stores whole
+    // 16-byte units (8 columns): half 0 the units q = 0, 1, half 1 the units
+    // q = 2, 3 (partial 8-byte stores wrote about 1.4x the output bytes)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = m0 + wm * 128 + i * 32 + r32;
+#pragma unroll
+      for (int j = 0; j < JB; j++) {
+        u32x2 pk[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) v[e] = kNv ? acc[i][j][4 * q + e] * st : acc[i][j][4 * q + e];
+          pk[q] = (u32x2){f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16),
+                          f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16)};
+        }
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+          const u32x2 keep = half ? pk[2 + a] : pk[a];  // unit q = 2 half + a, own 4 columns
+          const u32x2 send = half ? pk[a] : pk[2 + a];  // what the partner needs
+          const u32x2 got = {(unsigned)__shfl_xor((int)send.x, 32, 64), (unsigned)__shfl_xor((int)send.y, 32, 64)};
+          const u32x4 unit = half ? (u32x4){got.x, got.y, keep.x, keep.y} : (u32x4){keep.x, keep.y, got.x, got.y};
+          const int64_t col = n0 + wn * WCOLS + j * 32 + 8 * (2 * half + a);
+          if (row >= m || col >= n) continue;
+          uint16_t* dst = (uint16_t*)y + row * n + col;
+          if (col + 8 <= n && (n & 7) == 0) {
+            *(u32x4*)dst = unit;
+          } else {
+            const unsigned w[4] = {unit.x, unit.y, unit.z, unit.w};
+            for (int e = 0; e < 8 && col + e < n; e++) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t row = m0 + wm * 128 + i * 32 + r32;

@@ -552,7 +552,7 @@ def test_gemv_tiny_ref():
 @pytest.mark.parametrize("n,k,m", [(1, 32, 1), (17, 160, 2), (300, 4128, 4), (33, 96, 16), (65, 256, 17),
                                    (100, 2080, 5), (70, 4096, 8), (130, 8192, 16), (64, 6144, 11),
                                    (40, 512, 33), (129, 1024, 100), (300, 320, 130), (513, 64, 257),
-                                   (256, 1024, 512), (1, 64, 128)])
+                                   (256, 1024, 512), (1, 64, 128), (264, 256, 200)])
 def test_gemv_ragged_shapes(n, k, m):
     w = laplace_bf16(n * 13 + k, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(m).standard_normal((m, k)).astype(np.float32))
@@ -629,7 +629,8 @@ def test_gemv_decode_full_size_sampled(m):
 
 
 def test_nv_gemm_ragged():
-    for (n, k, m) in [(5, 16, 1), (40, 48, 3), (70, 272, 20), (256, 1024, 64), (300, 320, 130), (513, 64, 257)]:
+    for (n, k, m) in [(5, 16, 1), (40, 48, 3), (70, 272, 20), (256, 1024, 64), (300, 320, 130), (513, 64, 257),
+                      (264, 128, 136)]:
         w = laplace_bf16(n + k, n, k)
         x = synth.f32_to_bf16_bits(np.random.default_rng(k).standard_normal((m, k)).astype(np.float32))
         qo, so, go = assert_nv(w, None, f"nv gemm W {n}x{k}")
