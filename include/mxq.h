@@ -178,6 +178,12 @@ MXQ_API mxq_status mxq_gemm_w4a4(const uint8_t *aq, const uint8_t *as,
  * 0.  [Kimi K3 release format: MXFP4 weights with MXFP8 activations, "Low-
  * precision inference and MXFP4 quantization" page; mxfp8 scheme, infra-
  * guide sec. 4.2.]  Errors as mxq_gemm_w4a4.
+ * Accuracy: the instruction adds the products of each group of 8
+ * consecutive k aligned to the group's largest exponent E_g (the two codes'
+ * exponents summed) and truncated toward zero at 2^(E_g - 13), before the
+ * block scales and the fp32 accumulation (measured on gfx950), so a group
+ * can lose up to about 8 * 2^(E_g - 13) times its two block scales; with
+ * at most one nonzero activation per group the result is fp32-accurate.
  */
 MXQ_API mxq_status mxq_gemm_w4a8(const uint8_t *aq8, const uint8_t *as,
                          const uint8_t *bq, const uint8_t *bs, int64_t m,
