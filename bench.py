@@ -83,7 +83,7 @@ def quant_bytes(rows, k, in_bytes=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch
