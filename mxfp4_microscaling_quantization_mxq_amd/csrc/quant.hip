@@ -615,10 +615,27 @@ __global__ __launch_bounds__(256) void k_tf4_amax(const u32x4* __restrict__ x, i
 #pragma unroll
     for (int u = 0; u < kTf4U; u++) {
       rotate8<32>(v[u], lane);
-      float rv;
-      tf4_split(v[u], lane, rv);
+      // the block's largest |y| once the residual is removed is its second
+      // largest |y| counted with multiplicity: a running top two per lane,
+      // merged over the quad (|y| orders like its bits)
+      unsigned m1 = 0, m2 = 0;
 #pragma unroll
-      for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
+      for (int i = 0; i < 8; i++) {
+        const unsigned a = __float_as_uint(v[u][i]) & 0x7FFFFFFFu;
+        m2 = max(m2, min(m1, a));
+        m1 = max(m1, a);
+      }
+      {
+        const unsigned p1 = dpp_quad_xor1(m1), p2 = dpp_quad_xor1(m2);
+        m2 = max(min(m1, p1), max(m2, p2));
+        m1 = max(m1, p1);
+      }
+      {
+        const unsigned p1 = dpp_quad_xor2(m1), p2 = dpp_quad_xor2(m2);
+        m2 = max(min(m1, p1), max(m2, p2));
+        m1 = max(m1, p1);
+      }
+      m = max(m, m2);
     }
   }
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
