@@ -65,6 +65,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
+// The same 16-byte copy through a buffer resource (buffer_load_dwordx4 ...
+// lds): base and size in SGPRs, a 32-bit per-lane offset and a uniform
+// offset.  Measured about 3 % faster than the 64-bit-address form in the
+// block-scaled GEMM rings.
+constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
 __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }

@@ -201,6 +201,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   // scale copies: 16 B per row per stage pair; with 4 waves each wave copies
   // 64 rows of A and of B, with 8 waves waves 0-3 copy A and 4-7 copy B
   const int srow = NWV == 4 ? 64 * wave + lane : 64 * (wave & 3) + lane;
+  // codes through buffer resources over the tile's row panels (the launcher
+  // keeps every panel below 2^31 bytes); per-lane offsets fixed for the k loop
+  const __amdgpu_buffer_rsrc_t rA = panel_rsrc(aq + m0 * kq, rows_a * kq);
+  const __amdgpu_buffer_rsrc_t rB = panel_rsrc(bq + n0 * kq, rows_b * kq);
   const uint8_t* gsa = as + min(m0 + srow, m - 1) * ks;
   const uint8_t* gsb = bs + min(n0 + srow, n - 1) * ks;
   // lane offsets of the CJ code copies per operand (fixed for the k loop)
@@ -219,13 +223,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   // the end is clamped to the last one: a re-read into a slot nobody reads)
   auto issue_codes = [&](auto cb_tag, int s) {
     uint8_t* base = w4_codes<decltype(cb_tag)::value>();
-    const int sc = min(s, nstages - 1);
-    const uint8_t* srcA = aq + m0 * kq + (int64_t)sc * kSB;
-    const uint8_t* srcB = bq + n0 * kq + (int64_t)sc * kSB;
+    const unsigned soff = (unsigned)min(s, nstages - 1) * kSB;
 #pragma unroll
     for (int j = 0; j < CJ; j++) {
-      dma16(srcA + offa[j], base + (RPW * wave + 8 * j) * kSB);
-      dma16(srcB + offb[j], base + kBM * kSB + (RPW * wave + 8 * j) * kSB);
+      bdma16(rA, offa[j], soff, base + (RPW * wave + 8 * j) * kSB);
+      bdma16(rB, offb[j], soff, base + kBM * kSB + (RPW * wave + 8 * j) * kSB);
     }
   };
   // scales of stage pair p into scale slot SB: 16 B per row (2 copies per
@@ -441,7 +443,9 @@ constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
 template <int OUT>
 static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                             int64_t n, int64_t k, void* c, uint8_t* cs, hipStream_t st) {
-  if (k % 1024 == 0 && k >= 1024) {
+  // the ring addresses its row panels with 32-bit offsets: 256 rows * k/2
+  // bytes stay below 2^31 for k < 2^24
+  if (k % 1024 == 0 && k >= 1024 && k < (1 << 24)) {
     const unsigned tiles = (unsigned)(((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
     hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, OUT>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs, m,
                        n, k, c, cs);

@@ -171,8 +171,13 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_ring(const uint8_t* __restrict_
   // copy the A rows again (the same bytes to the same place)
   const bool sc_a = wave < 2 || wave >= 6;
   const int srow = sc_a ? 64 * (wave & 1) + lane : 64 * (wave - 2) + lane;
-  const uint8_t* gsc = sc_a ? as + min(m0 + srow, m - 1) * ks : bs + min(n0 + srow, n - 1) * ks;
   const int sdst = sc_a ? (64 * (wave & 1)) * 16 : kA8M * 16 + (64 * (wave - 2)) * 16;
+  // buffer resources over the tile's row panels (below 2^31 bytes: the
+  // launcher takes this kernel for k < 2^24 only)
+  const __amdgpu_buffer_rsrc_t rA = panel_rsrc(aq8 + m0 * k, rows_a * k);
+  const __amdgpu_buffer_rsrc_t rB = panel_rsrc(bq + n0 * kq, rows_b * kq);
+  const __amdgpu_buffer_rsrc_t rS = sc_a ? panel_rsrc(as + m0 * ks, rows_a * ks) : panel_rsrc(bs + n0 * ks, rows_b * ks);
+  const unsigned soff_row = (unsigned)(min(srow, sc_a ? rows_a - 1 : rows_b - 1) * ks);
   // code copies: wave w fills A rows 16 w .. 16 w + 15 (4 copies of 4 rows)
   // and B rows 32 w .. 32 w + 31 (4 copies of 8 rows); lane offsets fixed
   // for the k loop, the swizzle applied on the global side
@@ -188,19 +193,16 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_ring(const uint8_t* __restrict_
 
   auto issue_codes = [&](auto cb_tag, int s) {
     uint8_t* base = a8_codes<decltype(cb_tag)::value>();
-    const int sc = min(s, nstages - 1);
-    const uint8_t* srcA = aq8 + m0 * k + (int64_t)sc * kA8RowA;
-    const uint8_t* srcB = bq + n0 * kq + (int64_t)sc * kA8RowB;
+    const unsigned sc = (unsigned)min(s, nstages - 1);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      dma16(srcA + offa[j], base + (16 * wave + 4 * j) * kA8RowA);
-      dma16(srcB + offb[j], base + kA8M * kA8RowA + (32 * wave + 8 * j) * kA8RowB);
+      bdma16(rA, offa[j], sc * kA8RowA, base + (16 * wave + 4 * j) * kA8RowA);
+      bdma16(rB, offb[j], sc * kA8RowB, base + kA8M * kA8RowA + (32 * wave + 8 * j) * kA8RowB);
     }
   };
   auto issue_scales = [&](auto sb_tag, int p) {
     uint8_t* sbase = a8_scales<decltype(sb_tag)::value>();
-    const int pc = min(p, npairs - 1);
-    dma16(gsc + (int64_t)pc * 16, sbase + sdst);
+    bdma16(rS, soff_row, (unsigned)min(p, npairs - 1) * 16u, sbase + sdst);
   };
 
   f32x16 acc[2][2];
