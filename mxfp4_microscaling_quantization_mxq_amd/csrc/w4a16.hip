@@ -435,10 +435,10 @@ __global__ __launch_bounds__(256) void k_w4a16_decode_mfma(const uint8_t* __rest
 
 // ---------------------------------------------------------------------------
 // GEMM kernel (large m, k % 64 == 0): bf16 MFMA, MFMA-bound.
-// Block tile 256 (x rows) x 256 (weight rows), four waves of 128 x 128, each
-// a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 per 16-k step.  k advances in
-// stages of 64 through a ring of three LDS stages filled by direct
-// global -> LDS loads (global_load_lds_dwordx4):
+// Block tile 256 (x rows) x 256 (weight rows), eight waves of 128 x 64 (or
+// four of 128 x 128), each a grid of v_mfma_f32_32x32x16_bf16 per 16-k step.
+// k advances in stages of 64 through a ring of three LDS stages filled by
+// direct buffer -> LDS loads (buffer_load_dwordx4 ... lds):
 //   * x: 256 rows x 128 B per stage, 16-B unit u of row r stored at
 //     u ^ ((r >> 1) & 7) (conflict-free fragment reads);
 //   * weight codes: 256 rows x 32 B per stage, unit u at u ^ ((r >> 3) & 1).
@@ -467,6 +467,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 }
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
 }
 template <int N>
 __device__ __forceinline__ void gwait_vmcnt() {
@@ -889,20 +892,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     offx[j] = real ? (unsigned)xr * (unsigned)kx + ((unsigned)(lane ^ (xr & 15)) << 4) : 0u;
     xdst[j] = (real ? xr : MT + 1) * kDdXRowB;
   }
-  const uint8_t* gw0 = wq + n0 * kq;
-  const uint8_t* gs0 = ws + n0 * ks;
+  // buffer resources over the block's weight, scale and activation panels
+  // (32-bit lane offsets; the panels stay below 2^31 bytes for k <= 2^24)
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * kq, (unsigned)(rows_w * kq));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(ws + n0 * ks, (unsigned)(rows_w * ks));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (unsigned)(m * kx));
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
     DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
     const int sl0 = min(s, nst - 1);
-    const int sc = sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst;
-    const uint8_t* gw = gw0 + (unsigned)sc * (unsigned)kDdRowB;
+    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
-    for (int q = 0; q < 4; q++) gdma16(gw + offw[q], sl.w + (16 * wave + 4 * q) * kDdRowB);
-    gdma4(gs0 + (unsigned)sc * (unsigned)kDdScB + offs, sl.s + 16 * wave * kDdScB);
-    const uint8_t* gx = (const uint8_t*)x + (unsigned)sc * (unsigned)kDdXRowB;
+    for (int q = 0; q < 4; q++) bdma16(rw, offw[q], sc * kDdRowB, sl.w + (16 * wave + 4 * q) * kDdRowB);
+    bdma4(rs, offs, sc * kDdScB, sl.s + 16 * wave * kDdScB);
 #pragma unroll
-    for (int j = 0; j < XPW; j++) gdma16(gx + offx[j], sl.x + xdst[j]);
+    for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * kDdXRowB, sl.x + xdst[j]);
   };
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};

@@ -119,13 +119,14 @@ constexpr int kBM = 256, kBN = 256;  // block tile of the ring kernel
 // Ring kernel (k % 1024 == 0).  Block tile 256 x 256; each wave multiplies
 // 32 x 32 blocks on v_mfma_scale_f32_32x32x64_f8f6f4 (one lane = 32 k = one
 // MX block = one E8M0 operand byte).  Operands are fed by direct
-// global -> LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
-// LDS base + 16 i), no staging registers.  A stage is 256 k = 128 code bytes
-// per row, so every request is a whole 128-B line (half-line requests ran at
-// roughly half the L2 throughput); two stages of 64 KiB ring in LDS.
+// buffer -> LDS loads (buffer_load_dwordx4 ... lds: lane i's 16 bytes land
+// at LDS base + 16 i; the scales by the global-address form), no staging
+// registers.  A stage is 256 k = 128 code bytes per row, so every request is
+// a whole 128-B line (half-line requests ran at roughly half the L2
+// throughput); two stages of 64 KiB ring in LDS.
 //   * Operands are swapped (B rows feed the instruction's A side), so a lane
-//     holds four consecutive output columns and stores them as one 8-byte
-//     bf16 write.
+//     holds four consecutive output columns (the fp32 epilogue stores them
+//     as one 16-byte write; bf16 and MXFP4 outputs are staged in LDS).
 //   * Tiles are ordered per XCD: the blocks an XCD runs take a contiguous
 //     run of tile ids, grouped four tile rows deep for L2 reuse.
 //   * LDS rows are 128 B; unit u (16 B) of row r sits at u ^ ((r >> 1) & 7),

@@ -108,9 +108,10 @@ __global__ __launch_bounds__(256) void k_w4a8_direct(const uint8_t* __restrict__
 // E2M1 bytes per B row, 32 KiB each -- the same 64 KiB per stage as the
 // W4A4 ring, and the same MFMA time per stage (an instruction with an E4M3
 // operand issues at half the E2M1 rate, and the tile has half the outputs).
-//   * Operands are fed by direct global -> LDS loads (global_load_lds
-//     dwordx4: lane i's 16 bytes land at the LDS base + 16 i), two stage
-//     slots ring in LDS, every request covers whole 128-B lines.
+//   * Operands and scales are fed by direct buffer -> LDS loads
+//     (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at the LDS base +
+//     16 i), two stage slots ring in LDS, every request covers whole 128-B
+//     lines.
 //   * A rows (256 B = 16 units of 16 B): unit u of row r sits at
 //     u ^ (r & 15); B rows (128 B): unit u at u ^ ((r >> 1) & 7).  Either
 //     way the 16 rows that one 16-lane group reads hit distinct banks.
