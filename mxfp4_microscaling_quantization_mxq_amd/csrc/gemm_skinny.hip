@@ -1,0 +1,349 @@
+// gemm_skinny.hip -- block-scaled MFMA products with few activation rows
+// (m <= 128), MXFP4 weights times MXFP4 (W4A4) or MXFP8 (W4A8)
+// activations.  The weight stream decides the time, so the kernel is laid
+// out like the W4A16 decode ring rather than like an output tile.
+//
+// A 256 x 256 output tile spends the same MFMA schedule on 16 activation
+// rows as on 256, and a 28672-row weight gives it only 112 tiles for 256
+// CUs; measured, the W4A4 and W4A8 tile kernels took 53-69 us at every
+// m <= 256 on a 28672 x 8192 MXFP4 weight, against about 21 us for the
+// weight read itself.  Batch size picks the kernel [deployment guide,
+// sec. 5.2: small batches and large batches take different GEMM kernels].
+//
+// Instruction: V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the activations as
+// operand A (E2M1 or E4M3) and the weights as operand B (E2M1).  Lane l
+// holds row l % 16 of its operand in lane group g = l / 16:
+//   * E2M1: one 32-element block of the 128-k step (16 bytes, element 2j in
+//     the low nibble of byte j, as stored);
+//   * E4M3: k = 16 g .. 16 g + 15 (bytes 0-15) and 64 + 16 g .. +15 (bytes
+//     16-31) of the step, which is the E4M3 operand of the 32x32x64 form
+//     (measured) spread over four lane groups;
+// plus the E8M0 byte of block g of the step on either side.  The 16 x 16
+// fp32 result sits in lane l at column l % 16, rows 4 g + r of register r.
+// Step i of a stage covers stage k 128 i .. 128 i + 127 in order, so the
+// instruction's groups of 8 consecutive k are 8 consecutive k of the
+// operands (the E4M3 x E2M1 group sums are truncated; see the W4A8 entry
+// point).
+//
+//   * Block = NW waves; wave w owns WT 16-row weight tiles (rows n0 + 16 WT w
+//     ..) for all of k, which runs in stages of KS = 512 or 256 through an
+//     NR-deep LDS ring filled by buffer -> LDS copies.
+//   * The activation rows' codes and scales of a stage (MT rows, shared by
+//     all waves) ride in the same ring slot.  Every wave issues the same
+//     number of copies; surplus ones land in scratch rows, so the wait
+//     counts are compile-time constants.
+//   * Activation rows m..MT-1 of the operand hold stale or clamped data;
+//     they only reach output rows that are never stored.
+//   * LDS swizzle (applied on the global side): 16-byte unit v of row r at
+//     slot v ^ (r % S), S = min(16, units per row).  Any 8 consecutive lanes
+//     of a fragment read hit 8 distinct bank groups.
+//   * One s_barrier per stage, after the wave's own copies have landed.
+//   * Blocks start their k loop at staggered stages, (block / 8) mod nst,
+//     so that the blocks resident at one time read different column ranges.
+#include <type_traits>
+
+#include "mxq_device.h"
+#include "mxq_gemm_common.h"
+#include "mxq_launch.h"
+
+namespace mxq {
+
+// Stage geometry for KS k per stage (512 or 256) and activation format.
+template <int KS, bool kFp8>
+struct SkGeom {
+  static constexpr int RowB = KS / 2;               // E2M1 weight code bytes per row
+  static constexpr int U = RowB / 16;               // weight units per row (16 or 8)
+  static constexpr int RPI = 64 / U;                // weight rows per 1-KiB copy
+  static constexpr int XRowB = kFp8 ? KS : KS / 2;  // activation code bytes per row
+  static constexpr int XU = XRowB / 16;             // activation units per row
+  static constexpr int XRPI = 64 / XU;              // activation rows per 1-KiB copy
+  static constexpr int ScB = KS / 32;               // scale bytes per row
+  static constexpr int LPR = ScB / 4;               // lanes per row of a scale copy (4-byte lanes)
+  static constexpr int STEPS = KS / 128;            // MFMA steps per stage
+};
+constexpr int swz(int units) { return units < 16 ? units : 16; }
+
+// One ring slot.  Each slot is its own LDS variable and every slot index is
+// a compile-time constant, so the compiler can tell that reads of one slot
+// do not touch the slots whose copies are in flight.
+template <int MT, int NW, int WT, int KS, bool kFp8>
+struct SkSlot {
+  using G = SkGeom<KS, kFp8>;
+  uint8_t w[16 * WT * NW * G::RowB];     // weight codes
+  uint8_t x[(MT + G::XRPI) * G::XRowB];  // activation codes, one copy's worth of scratch rows
+  // Scales: a 256-byte region per 16 rows (one 64-lane dword copy), row r
+  // of a group at (r % 16) * ScB; with 8 scale bytes per row the upper half
+  // of a region is scratch.
+  uint8_t ws[WT * NW * 256];             // weight scales
+  uint8_t xs[(MT / 16 + 1) * 256];       // activation scales, one scratch region
+};
+template <int MT, int NW, int WT, int KS, bool kFp8, int B>
+__device__ __forceinline__ SkSlot<MT, NW, WT, KS, kFp8>& sk_slot() {
+  __shared__ __attribute__((aligned(1024))) SkSlot<MT, NW, WT, KS, kFp8> slot;
+  return slot;
+}
+
+// WT = 16-row weight tiles per wave: with two, every activation fragment
+// read from LDS feeds two MFMAs.
+template <bool kFp8, int MT, int NW, int WT, int NR, int KS, bool kBf16Out>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __restrict__ aq,
+                                                           const uint8_t* __restrict__ as,
+                                                           const uint8_t* __restrict__ bq,
+                                                           const uint8_t* __restrict__ bs, int64_t m,
+                                                           int64_t n, int64_t k, void* __restrict__ c) {
+  using G = SkGeom<KS, kFp8>;
+  using Slot = SkSlot<MT, NW, WT, KS, kFp8>;
+  constexpr int WR = 16 * WT;                        // weight rows per wave
+  constexpr int RB = WR * NW;                        // weight rows per block
+  constexpr int MTT = MT / 16;                       // 16-row activation tiles
+  constexpr int WC = WR / G::RPI;                    // weight code copies per wave
+  constexpr int XC = (MT / G::XRPI + NW - 1) / NW;   // activation code copies per wave
+  constexpr int XS = (MT / 16 + NW - 1) / NW;        // activation scale copies per wave (16 rows each)
+  constexpr int D = WC + WT + XC + XS;               // copies per wave per stage
+  constexpr int WSW = swz(G::U), XSW = swz(G::XU);   // swizzle periods
+  static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * RB;
+  const int rows_w = (int)min((int64_t)RB, n - n0);
+  const int64_t kq = k / 2, ks = k / 32, kx = kFp8 ? k : k / 2;
+  const int nst = (int)(k / KS);
+  const int rot = (int)((blockIdx.x / 8) % (unsigned)nst);
+
+  // Lane offsets of the copies, fixed for the whole k loop (a stage only
+  // moves the uniform offset).  Rows past the operand are clamped to its
+  // last row: the copy stays in bounds and fills an LDS row nobody stores.
+  unsigned offw[WC], offws[WT], offx[XC], offxs[XS];
+  int dx[XC], dxs[XS];
+#pragma unroll
+  for (int q = 0; q < WC; q++) {
+    const int row = WR * wave + G::RPI * q + lane / G::U;
+    const unsigned unit = (unsigned)((lane % G::U) ^ (row % WSW));
+    offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
+  }
+  // scale copies: 4 bytes per lane; lane i takes row (i mod 16 LPR) / LPR of
+  // the group, dword i mod LPR, so lanes past 16 LPR repeat the group into
+  // the region's scratch half
+  const int srow = (lane % (16 * G::LPR)) / G::LPR;
+  const unsigned spart = 4u * (unsigned)(lane % G::LPR);
+#pragma unroll
+  for (int r = 0; r < WT; r++)
+    offws[r] = (unsigned)min(WR * wave + 16 * r + srow, rows_w - 1) * (unsigned)ks + spart;
+#pragma unroll
+  for (int j = 0; j < XC; j++) {
+    const int a = wave + NW * j;  // copy slot (wave-uniform): activation rows XRPI a ..
+    const int row = G::XRPI * a + lane / G::XU;
+    const unsigned unit = (unsigned)((lane % G::XU) ^ (row % XSW));
+    offx[j] = (unsigned)min((int64_t)row, m - 1) * (unsigned)kx + (unit << 4);
+    dx[j] = (G::XRPI * a < MT ? G::XRPI * a : MT) * G::XRowB;
+  }
+#pragma unroll
+  for (int j = 0; j < XS; j++) {
+    const int a = wave + NW * j;  // activation rows 16a .. 16a+15
+    const int row = 16 * a + srow;
+    offxs[j] = (unsigned)min((int64_t)row, m - 1) * (unsigned)ks + spart;
+    dxs[j] = (16 * a < MT ? a : MT / 16) * 256;
+  }
+  const __amdgpu_buffer_rsrc_t rw = panel_rsrc(bq + n0 * kq, rows_w * kq);
+  const __amdgpu_buffer_rsrc_t rws = panel_rsrc(bs + n0 * ks, rows_w * ks);
+  const __amdgpu_buffer_rsrc_t rx = panel_rsrc(aq, m * kx);
+  const __amdgpu_buffer_rsrc_t rxs = panel_rsrc(as, m * ks);
+
+  // Copies of stage s into ring slot B.  A stage past the end is clamped to
+  // the last one (a re-read into a slot nobody reads), so every step issues
+  // the same copies.
+  auto issue = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    Slot& sl = sk_slot<MT, NW, WT, KS, kFp8, B>();
+    const int sl0 = min(s, nst - 1);
+    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+#pragma unroll
+    for (int q = 0; q < WC; q++)
+      bdma16(rw, offw[q], sc * G::RowB, sl.w + (WR * wave + G::RPI * q) * G::RowB);
+#pragma unroll
+    for (int r = 0; r < WT; r++) bdma4(rws, offws[r], sc * G::ScB, sl.ws + 256 * (WT * wave + r));
+#pragma unroll
+    for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
+#pragma unroll
+    for (int j = 0; j < XS; j++) bdma4(rxs, offxs[j], sc * G::ScB, sl.xs + dxs[j]);
+  };
+
+  f32x4 acc[WT][MTT];
+#pragma unroll
+  for (int r = 0; r < WT; r++)
+#pragma unroll
+    for (int t = 0; t < MTT; t++) acc[r][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int wrow = WR * wave + col;  // this lane's block weight row in tile 0 (+16 r in tile r)
+  // scale bytes of a row as words: word i holds blocks 4i .. 4i+3
+  auto scale_words = [&](const uint8_t* p, unsigned (&wds)[G::STEPS]) {
+    if constexpr (G::STEPS == 4) {
+      const u32x4 v = *(const u32x4*)p;
+      wds[0] = v.x; wds[1] = v.y; wds[2] = v.z; wds[3] = v.w;
+    } else {
+      const u32x2 v = *(const u32x2*)p;
+      wds[0] = v.x; wds[1] = v.y;
+    }
+  };
+  // activation fragment of step i from an activation row r, r % 16 == col
+  auto x_fragment = [&](const uint8_t* row, int i) -> i32x8 {
+    if constexpr (kFp8) {
+      const u32x4 lo = *(const u32x4*)(row + (((8 * i + g) ^ (col % XSW)) << 4));
+      const u32x4 hi = *(const u32x4*)(row + (((8 * i + 4 + g) ^ (col % XSW)) << 4));
+      return (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const u32x4 v = *(const u32x4*)(row + (((4 * i + g) ^ (col % XSW)) << 4));
+      return (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+  };
+  auto compute = [&](auto slot_tag) {
+    constexpr int B = decltype(slot_tag)::value;
+    const Slot& sl = sk_slot<MT, NW, WT, KS, kFp8, B>();
+    unsigned wss[WT][G::STEPS], xss[MTT][G::STEPS];
+#pragma unroll
+    for (int r = 0; r < WT; r++) scale_words(sl.ws + 256 * (WT * wave + r) + col * G::ScB, wss[r]);
+#pragma unroll
+    for (int t = 0; t < MTT; t++) scale_words(sl.xs + 256 * t + col * G::ScB, xss[t]);
+#pragma unroll
+    for (int i = 0; i < G::STEPS; i++) {
+      const int wslot = ((4 * i + g) ^ (col % WSW)) << 4;  // weight unit 4i+g of a row r, r % 16 == col
+      i32x8 wf[WT];
+      int sw[WT];
+#pragma unroll
+      for (int r = 0; r < WT; r++) {
+        const u32x4 cw = *(const u32x4*)(sl.w + (wrow + 16 * r) * G::RowB + wslot);
+        wf[r] = (i32x8){(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
+        sw[r] = (int)((wss[r][i] >> (8 * g)) & 0xFFu);
+      }
+#pragma unroll
+      for (int t = 0; t < MTT; t++) {
+        const i32x8 xf = x_fragment(sl.x + (16 * t + col) * G::XRowB, i);
+        const int sx = (int)((xss[t][i] >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int r = 0; r < WT; r++)
+          acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf[r], acc[r][t], kFp8 ? kFmtFp8 : kFmtFp4,
+                                                                      kFmtFp4, 0, sx, 0, sw[r]);
+      }
+    }
+  };
+
+  // One stage: wait for its copies (NR - 2 later stages may stay in
+  // flight) and for this wave's reads of the slot about to be refilled,
+  // meet the other waves, refill, multiply.
+  auto step = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    constexpr int N = (NR - 2) * D;
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
+    if (s < nst) compute(slot_tag);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % NR>;
+  using I2 = std::integral_constant<int, 2 % NR>;
+  using I3 = std::integral_constant<int, 3 % NR>;
+  issue(I0{}, 0);
+  if (NR > 2) issue(I1{}, 1);
+  if (NR > 3) issue(I2{}, 2);
+  step(I0{}, 0);
+  for (int s = 1; s < nst; s += NR) {
+    step(I1{}, s);
+    if (NR > 2) step(I2{}, s + 1);
+    if (NR > 3) step(I3{}, s + 2);
+    step(I0{}, s + NR - 1);
+  }
+  wait_vmcnt<0>();
+
+  // lane holds c[16t + 4g + e][n0 + wrow + 16r]
+#pragma unroll
+  for (int r = 0; r < WT; r++) {
+    const int64_t nn = n0 + wrow + 16 * r;
+    if (nn >= n) continue;
+#pragma unroll
+    for (int t = 0; t < MTT; t++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int64_t mm = 16 * t + 4 * g + e;
+        if (mm >= m) continue;
+        if (kBf16Out)
+          ((uint16_t*)c)[mm * n + nn] = f32_to_bf16_rne(acc[r][t][e]);
+        else
+          ((float*)c)[mm * n + nn] = acc[r][t][e];
+      }
+  }
+}
+
+template <bool kFp8, int MT, int NW, int WT, int NR, int KS>
+static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                      int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  constexpr int RB = 16 * WT * NW;
+  const dim3 grid((unsigned)((n + RB - 1) / RB));
+  if (bf16_out)
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, WT, NR, KS, true>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs,
+                       m, n, k, c);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, WT, NR, KS, false>), grid, dim3(64 * NW), 0, st, aq, as, bq,
+                       bs, m, n, k, c);
+}
+
+// Launch configurations <MT, NW, WT, NR, KS> per activation tile.  The LDS
+// ring holds at most 160 KiB: the 128-row tile of E2M1 activations fits
+// two 512-k stages, the 64- and 128-row E4M3 tiles take 256-k stages.
+#ifndef MXQ_SK4_C16
+#define MXQ_SK4_C16 16, 7, 1, 3, 512
+#endif
+#ifndef MXQ_SK4_C32
+#define MXQ_SK4_C32 32, 7, 1, 3, 512
+#endif
+#ifndef MXQ_SK4_C64
+#define MXQ_SK4_C64 64, 7, 1, 3, 512
+#endif
+#ifndef MXQ_SK4_C128
+#define MXQ_SK4_C128 128, 7, 1, 2, 512
+#endif
+#ifndef MXQ_SK8_C16
+#define MXQ_SK8_C16 16, 7, 1, 3, 512
+#endif
+#ifndef MXQ_SK8_C32
+#define MXQ_SK8_C32 32, 7, 1, 3, 512
+#endif
+#ifndef MXQ_SK8_C64
+#define MXQ_SK8_C64 64, 7, 1, 4, 256
+#endif
+#ifndef MXQ_SK8_C128
+#define MXQ_SK8_C128 128, 7, 1, 3, 256
+#endif
+
+bool gemm_skinny_applies(int64_t m, int64_t k) {
+  // 32-bit copy offsets: a weight panel of at most 224 rows and a 128-row
+  // activation panel stay below 2^31 bytes for k <= 2^24
+  return m >= 1 && m <= 128 && k % 512 == 0 && k <= (1 << 24);
+}
+
+hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                              int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  if (m <= 16)
+    launch_sk<false, MXQ_SK4_C16>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 32)
+    launch_sk<false, MXQ_SK4_C32>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 64)
+    launch_sk<false, MXQ_SK4_C64>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
+  else
+    launch_sk<false, MXQ_SK4_C128>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                              int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  if (m <= 16)
+    launch_sk<true, MXQ_SK8_C16>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 32)
+    launch_sk<true, MXQ_SK8_C32>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 64)
+    launch_sk<true, MXQ_SK8_C64>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  else
+    launch_sk<true, MXQ_SK8_C128>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

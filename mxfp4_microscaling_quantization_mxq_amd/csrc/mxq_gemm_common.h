@@ -11,6 +11,9 @@ namespace mxq {
 // output: the quantizer is the same device function).
 constexpr int kOutF32 = 0, kOutBf16 = 1, kOutMx = 2;
 
+// Operand format codes of the f8f6f4 block-scaled MFMA (E4M3, E2M1).
+constexpr int kFmtFp8 = 0, kFmtFp4 = 4;
+
 // Quantizes a bf16 output tile staged in LDS and stores its codes and E8M0
 // scales.  The tile has ROWS rows of COLS bytes (COLS / 16 units of 8 bf16);
 // rows [0, 128) sit in lo and [128, ROWS) in hi (two LDS variables when the
@@ -75,6 +78,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const void* base, i
 }
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+// 4-byte form: the copy places one dword per lane (LDS base + 4 i).
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)voff, (int)soff, 0, 0);
 }
 __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);

@@ -43,6 +43,14 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
 hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
 
+// W4A4 and W4A8 for few activation rows (weight-stream bound), used where
+// gemm_skinny_applies: m <= 128, k % 512 == 0, k <= 2^24.
+bool gemm_skinny_applies(int64_t m, int64_t k);
+hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                              int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
+hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                              int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
+
 // W4A4 with the product rounded to bf16 and quantized to MXFP4 along n in
 // the epilogue: cq[m][n/2], cs[m][n/32]; n % 32 == 0.
 hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,

@@ -444,6 +444,10 @@ constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
 template <int OUT>
 static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                             int64_t n, int64_t k, void* c, uint8_t* cs, hipStream_t st) {
+  if (OUT != kOutMx && gemm_skinny_applies(m, k)) {
+    launch_w4a4_skinny(aq, as, bq, bs, m, n, k, c, OUT == kOutBf16, st);
+    return;
+  }
   // the ring addresses its row panels with 32-bit offsets: 256 rows * k/2
   // bytes stay below 2^31 for k < 2^24
   if (k % 1024 == 0 && k >= 1024 && k < (1 << 24)) {

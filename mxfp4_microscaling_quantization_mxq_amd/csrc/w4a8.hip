@@ -23,7 +23,6 @@
 
 namespace mxq {
 
-constexpr int kFmtFp8 = 0, kFmtFp4 = 4;  // f8f6f4 operand format codes (E4M3, E2M1)
 
 // Block tile 128 x 128 of four 64 x 64 wave tiles (2 x 2 MFMAs of 32 x 32
 // per 64-k step); every wave reads its own fragments from global memory
@@ -368,6 +367,7 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_ring(const uint8_t* __restrict_
 
 hipError_t launch_w4a8(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  if (gemm_skinny_applies(m, k)) return launch_w4a8_skinny(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
   // the ring's per-lane copy offsets are 32-bit: 128 rows * k < 2^32
   if (k % 1024 == 0 && k >= 1024 && k < (1 << 24)) {
     const unsigned tiles = (unsigned)(((m + kA8M - 1) / kA8M) * ((n + kA8N - 1) / kA8N));

@@ -254,6 +254,32 @@ def test_w4a8_one_term_per_group(m, n, k):
     w4a8_case(a, b, f"w4a8 sparse {m}x{n}x{k}", exact_groups=True)
 
 
+# Few activation rows (m <= 128, k % 512 == 0) take the weight-stream kernel
+# (16x16x128 instruction); the sparse cases pin its E4M3 operand layout
+# against the tight bound.
+SKINNY8_SHAPES = [(1, 1000, 512), (7, 2000, 1536), (16, 1800, 4096), (30, 1121, 2048), (33, 2500, 1024),
+                  (64, 999, 3072), (65, 1500, 2560), (128, 1793, 2048), (100, 113, 512), (2, 7, 512)]
+
+
+@pytest.mark.parametrize("m,n,k", SKINNY8_SHAPES)
+def test_w4a8_skinny_ragged(m, n, k):
+    rng = np.random.default_rng(5 * m + n + k)
+    a = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * np.exp2(rng.integers(-6, 7, size=(m, 1)))).astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    w4a8_case(a, b, f"w4a8 skinny {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", SKINNY8_SHAPES[::2] + [(128, 300, 1024)])
+def test_w4a8_skinny_one_term_per_group(m, n, k):
+    rng = np.random.default_rng(m * 13 + n * 5 + k)
+    a = rng.standard_normal((m, k)) * np.exp2(rng.integers(-6, 7, size=(m, 1)))
+    keep = np.zeros((m, k // 8, 8), dtype=bool)
+    keep[np.arange(m)[:, None], np.arange(k // 8)[None, :], rng.integers(0, 8, size=(m, k // 8))] = True
+    a = synth.f32_to_bf16_bits(np.where(keep.reshape(m, k), a, 0.0).astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    w4a8_case(a, b, f"w4a8 skinny sparse {m}x{n}x{k}", exact_groups=True)
+
+
 def test_w4a8_all_code_pairs_exact():
     """Every E4M3 code against every E2M1 code with unit scales: C[i][j] =
     E4M3(i) * E2M1(j) exactly (one product per output, k = 64)."""
@@ -693,6 +719,58 @@ def test_w4a4_ragged(m, n, k):
     a = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
     b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
     w4a4_case(a, b, f"w4a4 {m}x{n}x{k}")
+
+
+# Few activation rows (m <= 128, k % 512 == 0) take the weight-stream kernel:
+# every activation tile (16, 32, 64, 128 rows), odd and even stage counts,
+# weight rows ragged across its 112-row blocks, and more than eight blocks
+# so that the staggered k start takes several values.
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 512), (5, 2000, 1536), (16, 1800, 4096), (17, 1121, 2048),
+                                   (33, 2500, 1024), (64, 999, 3072), (65, 1500, 2560), (128, 1793, 2048),
+                                   (100, 113, 512), (2, 7, 512), (48, 3000, 5120)])
+def test_w4a4_skinny_ragged(m, n, k):
+    rng = np.random.default_rng(7 * m + n + k)
+    a = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * np.exp2(rng.integers(-4, 5, size=(m, 1))))
+                               .astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    w4a4_case(a, b, f"w4a4 skinny {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [16, 128])
+def test_w4a4_skinny_full_size_sampled(m):
+    """The 28672 x 8192 decode weight against m quantized activation rows."""
+    _, qo, so = decode_weight()
+    _, x = synth.decode_gemv(m)
+    qx, sx = assert_mx_codes(x, f"skinny m={m} activations")
+    n = qo.shape[0]
+    args = (dev(qx), dev(sx), dev(qo), dev(so))
+    c = host(mxq.gemm_w4a4(*args, torch.bfloat16))
+    c2 = host(mxq.gemm_w4a4(*args, torch.bfloat16))
+    assert np.array_equal(c, c2), "run-to-run determinism"
+    rng = np.random.default_rng(300 + m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=384, replace=False), [0, n - 1]]))
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qx, sx), oracle.mx_dequantize(qo[cols], so[cols]))
+    worst = check_product(c[:, cols], yref, S, True, f"w4a4 skinny m={m}")
+    say(f"w4a4 skinny m={m}: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
+
+
+@pytest.mark.parametrize("m", [16, 128])
+def test_w4a8_skinny_full_size_sampled(m):
+    """The 28672 x 8192 decode weight against m MXFP8 activation rows."""
+    _, qo, so = decode_weight()
+    _, x = synth.decode_gemv(m)
+    qx, sx = assert_mx8_codes(x, f"skinny m={m} MXFP8 activations")
+    n = qo.shape[0]
+    args = (dev(qx), dev(sx), dev(qo), dev(so))
+    c = host(mxq.gemm_w4a8(*args, torch.bfloat16))
+    c2 = host(mxq.gemm_w4a8(*args, torch.bfloat16))
+    assert np.array_equal(c, c2), "run-to-run determinism"
+    rng = np.random.default_rng(400 + m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=384, replace=False), [0, n - 1]]))
+    yref, S = oracle.gemm_nt(oracle.mx8_dequantize(qx, sx), oracle.mx_dequantize(qo[cols], so[cols]))
+    extra = w4a8_block_sum_allowance(qx, sx, qo[cols], so[cols])
+    worst = check_product(c[:, cols], yref, S, True, f"w4a8 skinny m={m}", extra)
+    say(f"w4a8 skinny m={m}: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
 
 
 def test_w4a4_all_16x16_code_products_exact():
