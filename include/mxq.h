@@ -207,6 +207,28 @@ MXQ_API mxq_status mxq_gemm_w4a4_quant(const uint8_t *aq, const uint8_t *as,
                                hipStream_t stream);
 
 /*
+ * W4A4 product from bf16 activations quantized inside the kernel:
+ * c[m][n] = sum_k MXFP4(x)[m][k] * B_hat[n][k], where MXFP4(x) is exactly
+ * what mxq_quantize writes for x (the same quantizer runs on the same
+ * values), so c is bit-identical to mxq_quantize followed by mxq_gemm_w4a4.
+ * The activation codes never reach memory.  [TransFP4 page sec. 2.5: format
+ * conversion belongs in the GEMM's load stage, not in a separate
+ * intermediate tensor; "FP4 quantization analysis" page, QuTLASS kernel
+ * section: quantization fused into the GEMM kernels.]
+ * x bf16 [m][k]; B = (bq[n][k/2], bs[n][k/32]); fp32 accumulation; c
+ * written as cdt.  For decode-sized batches only: every block of 112
+ * weight rows quantizes the bf16 activation tile again, which pays while the
+ * weight stream dominates.  1 <= m <= 16, k % 512 == 0, k <= 2^24, else
+ * MXQ_ERROR_INVALID_VALUE (larger batches: mxq_quantize once, then
+ * mxq_gemm_w4a4, which is faster there).  m == 0 or n == 0: no-op; k == 0
+ * writes zeros.  Errors otherwise as mxq_gemm_w4a4.
+ */
+MXQ_API mxq_status mxq_gemm_w4a4_dynamic(const void *x, const uint8_t *bq,
+                                 const uint8_t *bs, int64_t m, int64_t n,
+                                 int64_t k, void *c, mxq_dtype cdt,
+                                 hipStream_t stream);
+
+/*
  * NVFP4 quantize.  x[rows][k] (xdt) -> q[rows][k/2] packed E2M1 codes,
  * s[rows][k/16] E4M3 block-scale codes, and the fp32 tensor scale *gscale
  * (a single float in device memory, the dequantization multiplier).

@@ -38,8 +38,7 @@
 //     slot v ^ (r % S), S = min(16, units per row).  Any 8 consecutive lanes
 //     of a fragment read hit 8 distinct bank groups.
 //   * One s_barrier per stage, after the wave's own copies have landed.
-//   * Blocks start their k loop at staggered stages, (block / 8) mod nst,
-//     so that the blocks resident at one time read different column ranges.
+//   * Blocks start their k loop at staggered k (skinny_rotation).
 #include <type_traits>
 
 #include "mxq_device.h"
@@ -62,6 +61,15 @@ struct SkGeom {
   static constexpr int STEPS = KS / 128;            // MFMA steps per stage
 };
 constexpr int swz(int units) { return units < 16 ? units : 16; }
+
+// First stage of a block's k loop: blocks start at staggered k, (block / 8)
+// mod (k / 512) chunks of 512, so that the blocks resident at one time read
+// different column ranges.  Counted in 512-k chunks, the k order of every
+// output is the same for either stage length.
+template <int KS>
+__device__ __forceinline__ int skinny_rotation(int64_t k) {
+  return (int)((blockIdx.x / 8) % (unsigned)(k / 512)) * (512 / KS);
+}
 
 // One ring slot.  Each slot is its own LDS variable and every slot index is
 // a compile-time constant, so the compiler can tell that reads of one slot
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = k / 32, kx = kFp8 ? k : k / 2;
   const int nst = (int)(k / KS);
-  const int rot = (int)((blockIdx.x / 8) % (unsigned)nst);
+  const int rot = skinny_rotation<KS>(k);
 
   // Lane offsets of the copies, fixed for the whole k loop (a stage only
   // moves the uniform offset).  Rows past the operand are clamped to its
@@ -286,6 +294,211 @@ static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, c
                        bs, m, n, k, c);
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 with the activations quantized in the kernel (MXFP4 of bf16 x, the
+// quantizer of mxq_quantize): the bf16 activation rows of a stage ride in
+// the ring instead of codes, and the block quantizes them once per stage
+// into a single MXFP4 tile that the MFMAs then read exactly as above.
+//   * After the stage barrier and the refill copies, lane q of the block
+//     takes MX blocks q, q + 64 NW, ... of the stage (one whole 32-element
+//     block per lane: mx_quantize_lane_bf16), writes its 16 code bytes and
+//     E8M0 byte into the tile, and a second barrier publishes the tile.
+//   * The tile is single: the next stage's quantization starts after the
+//     next stage barrier, which every wave reaches only once its reads of
+//     the tile are complete.
+//   * Blocks of 112 weight rows and the k order of skinny_rotation, as in
+//     the W4A4 kernel for the same m: the product is bit-identical to
+//     mxq_quantize followed by mxq_gemm_w4a4.
+template <int MT, int NW, int KS>
+struct SkDynSlot {
+  using G = SkGeom<KS, false>;
+  static constexpr int XRowB = 2 * KS;        // bf16 bytes per activation row
+  static constexpr int XRPI = 1024 / XRowB;   // activation rows per 1-KiB copy (1 or 2)
+  uint8_t w[16 * NW * G::RowB];               // weight codes
+  uint8_t x[(MT + XRPI) * XRowB];             // bf16 activation rows, one copy's worth of scratch
+  uint8_t ws[NW * 256];                       // weight scales (256-byte region per 16 rows)
+};
+template <int MT, int NW, int KS, int B>
+__device__ __forceinline__ SkDynSlot<MT, NW, KS>& sk_dyn_slot() {
+  __shared__ __attribute__((aligned(1024))) SkDynSlot<MT, NW, KS> slot;
+  return slot;
+}
+template <int MT, int KS>
+struct SkDynTile {
+  uint8_t x[MT * KS / 2];      // MXFP4 codes, unit b of row r at slot b ^ (r % 16)
+  uint8_t xs[MT / 16 * 256];   // E8M0 codes, a 256-byte region per 16 rows
+};
+template <int MT, int KS>
+__device__ __forceinline__ SkDynTile<MT, KS>& sk_dyn_tile() {
+  __shared__ __attribute__((aligned(1024))) SkDynTile<MT, KS> tile;
+  return tile;
+}
+
+template <int MT, int NW, int NR, int KS, bool kBf16Out>
+__global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16_t* __restrict__ x,
+                                                                   const uint8_t* __restrict__ bq,
+                                                                   const uint8_t* __restrict__ bs, int64_t m,
+                                                                   int64_t n, int64_t k, void* __restrict__ c) {
+  using G = SkGeom<KS, false>;
+  using Slot = SkDynSlot<MT, NW, KS>;
+  constexpr int RB = 16 * NW;                         // weight rows per block
+  constexpr int MTT = MT / 16;                        // 16-row activation tiles
+  constexpr int WC = 16 / G::RPI;                     // weight code copies per wave
+  constexpr int XU = Slot::XRowB / 16;                // 16-byte units per bf16 row
+  constexpr int XC = (MT / Slot::XRPI + NW - 1) / NW; // activation copies per wave
+  constexpr int D = WC + 1 + XC;                      // copies per wave per stage
+  constexpr int BPR = KS / 32;                        // MX blocks per row per stage
+  constexpr int NB = MT * BPR;                        // MX blocks per stage
+  constexpr int QPL = (NB + 64 * NW - 1) / (64 * NW); // blocks each lane quantizes
+  constexpr int WSW = swz(G::U);
+  static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * RB;
+  const int rows_w = (int)min((int64_t)RB, n - n0);
+  const int64_t kq = k / 2, ks = k / 32, kx = 2 * k;
+  const int nst = (int)(k / KS);
+  const int rot = skinny_rotation<KS>(k);
+
+  unsigned offw[WC], offx[XC];
+  int dx[XC];
+#pragma unroll
+  for (int q = 0; q < WC; q++) {
+    const int row = 16 * wave + G::RPI * q + lane / G::U;
+    const unsigned unit = (unsigned)((lane % G::U) ^ (row % WSW));
+    offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
+  }
+  const int srow = (lane % (16 * G::LPR)) / G::LPR;
+  const unsigned offws = (unsigned)min(16 * wave + srow, rows_w - 1) * (unsigned)ks + 4u * (unsigned)(lane % G::LPR);
+#pragma unroll
+  for (int j = 0; j < XC; j++) {
+    const int a = wave + NW * j;  // copy slot (wave-uniform): activation rows XRPI a ..
+    const int row = Slot::XRPI * a + lane / XU;
+    offx[j] = (unsigned)min((int64_t)row, m - 1) * (unsigned)kx + ((unsigned)(lane % XU) << 4);
+    dx[j] = (Slot::XRPI * a < MT ? Slot::XRPI * a : MT) * Slot::XRowB;
+  }
+  const __amdgpu_buffer_rsrc_t rw = panel_rsrc(bq + n0 * kq, rows_w * kq);
+  const __amdgpu_buffer_rsrc_t rws = panel_rsrc(bs + n0 * ks, rows_w * ks);
+  const __amdgpu_buffer_rsrc_t rx = panel_rsrc(x, m * kx);
+
+  auto issue = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
+    const int sl0 = min(s, nst - 1);
+    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+#pragma unroll
+    for (int q = 0; q < WC; q++)
+      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+    bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
+#pragma unroll
+    for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * Slot::XRowB, sl.x + dx[j]);
+  };
+
+  SkDynTile<MT, KS>& tile = sk_dyn_tile<MT, KS>();
+  auto quantize = [&](auto slot_tag) {
+    constexpr int B = decltype(slot_tag)::value;
+    const Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
+#pragma unroll
+    for (int j = 0; j < QPL; j++) {
+      const int q = tid + 64 * NW * j;
+      if (NB % (64 * NW) == 0 || q < NB) {
+        const int r = q / BPR, b = q % BPR;
+        bf16x8 xb[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) xb[u] = *(const bf16x8*)(sl.x + r * Slot::XRowB + (4 * b + u) * 16);
+        unsigned code;
+        const u32x4 codes = mx_quantize_lane_bf16(xb, &code);
+        *(u32x4*)(tile.x + r * G::RowB + ((b ^ (r % WSW)) << 4)) = codes;
+        tile.xs[(r / 16) * 256 + (r % 16) * G::ScB + b] = (uint8_t)code;
+      }
+    }
+  };
+
+  f32x4 acc[MTT];
+#pragma unroll
+  for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int wrow = 16 * wave + col;
+  auto compute = [&](auto slot_tag) {
+    constexpr int B = decltype(slot_tag)::value;
+    const Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
+    unsigned wss[G::STEPS], xss[MTT][G::STEPS];
+    auto words = [&](const uint8_t* p, unsigned (&wds)[G::STEPS]) {
+      if constexpr (G::STEPS == 4) {
+        const u32x4 v = *(const u32x4*)p;
+        wds[0] = v.x; wds[1] = v.y; wds[2] = v.z; wds[3] = v.w;
+      } else {
+        const u32x2 v = *(const u32x2*)p;
+        wds[0] = v.x; wds[1] = v.y;
+      }
+    };
+    words(sl.ws + 256 * wave + col * G::ScB, wss);
+#pragma unroll
+    for (int t = 0; t < MTT; t++) words(tile.xs + 256 * t + col * G::ScB, xss[t]);
+#pragma unroll
+    for (int i = 0; i < G::STEPS; i++) {
+      const int slot = ((4 * i + g) ^ (col % WSW)) << 4;
+      const u32x4 cw = *(const u32x4*)(sl.w + wrow * G::RowB + slot);
+      const i32x8 wf = {(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
+      const int sw = (int)((wss[i] >> (8 * g)) & 0xFFu);
+#pragma unroll
+      for (int t = 0; t < MTT; t++) {
+        const u32x4 cx = *(const u32x4*)(tile.x + (16 * t + col) * G::RowB + slot);
+        const i32x8 xf = {(int)cx.x, (int)cx.y, (int)cx.z, (int)cx.w, 0, 0, 0, 0};
+        const int sx = (int)((xss[t][i] >> (8 * g)) & 0xFFu);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf, acc[t], kFmtFp4, kFmtFp4, 0, sx, 0, sw);
+      }
+    }
+  };
+
+  // One stage: wait for its copies and for this wave's LDS reads, meet,
+  // refill, quantize the stage's activations into the tile, meet again,
+  // multiply.
+  auto step = [&](auto slot_tag, int s) {
+    constexpr int B = decltype(slot_tag)::value;
+    constexpr int N = (NR - 2) * D;
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
+    if (s < nst) {
+      quantize(slot_tag);
+      __builtin_amdgcn_s_waitcnt((15 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      compute(slot_tag);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % NR>;
+  using I2 = std::integral_constant<int, 2 % NR>;
+  using I3 = std::integral_constant<int, 3 % NR>;
+  issue(I0{}, 0);
+  if (NR > 2) issue(I1{}, 1);
+  if (NR > 3) issue(I2{}, 2);
+  step(I0{}, 0);
+  for (int s = 1; s < nst; s += NR) {
+    step(I1{}, s);
+    if (NR > 2) step(I2{}, s + 1);
+    if (NR > 3) step(I3{}, s + 2);
+    step(I0{}, s + NR - 1);
+  }
+  wait_vmcnt<0>();
+
+  const int64_t nn = n0 + wrow;
+  if (nn < n) {
+#pragma unroll
+    for (int t = 0; t < MTT; t++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int64_t mm = 16 * t + 4 * g + e;
+        if (mm >= m) continue;
+        if (kBf16Out)
+          ((uint16_t*)c)[mm * n + nn] = f32_to_bf16_rne(acc[t][e]);
+        else
+          ((float*)c)[mm * n + nn] = acc[t][e];
+      }
+  }
+}
+
 // Launch configurations <MT, NW, WT, NR, KS> per activation tile.  The LDS
 // ring holds at most 160 KiB: the 128-row tile of E2M1 activations fits
 // two 512-k stages, the 64- and 128-row E4M3 tiles take 256-k stages.
@@ -343,6 +556,31 @@ hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8
     launch_sk<true, MXQ_SK8_C64>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
   else
     launch_sk<true, MXQ_SK8_C128>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  return hipGetLastError();
+}
+
+template <int MT, int NW, int NR, int KS>
+static void launch_skd(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n, int64_t k,
+                       void* c, bool bf16_out, hipStream_t st) {
+  const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
+  if (bf16_out)
+    hipLaunchKernelGGL((k_w4a4_dynamic_skinny<MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
+                       k, c);
+  else
+    hipLaunchKernelGGL((k_w4a4_dynamic_skinny<MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
+                       k, c);
+}
+
+// Up to 16 activation rows.  Measured on a 28672 x 8192 weight against
+// mxq_quantize + the W4A4 kernel: 22.8 vs 24.5 us at m = 1, 25.0 vs 25.0 us
+// at m = 16, but 33.5 vs 27.2 us at m = 32 and 50.6 vs 29.9 us at m = 64,
+// where every block pulls a bf16 tile (4x the bytes of its codes) through
+// the same copy path as the weights.
+bool w4a4_dynamic_applies(int64_t m, int64_t k) { return m <= 16 && gemm_skinny_applies(m, k); }
+
+hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
+                               int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  launch_skd<16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
   return hipGetLastError();
 }
 

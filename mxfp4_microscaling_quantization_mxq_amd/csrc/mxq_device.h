@@ -135,4 +135,32 @@ __device__ __forceinline__ unsigned mx_quantize_quad_bf16(bf16x8 xb, unsigned* c
   return out;
 }
 
+// The same quantizer with one lane holding the whole block: elements
+// 8j .. 8j+7 in xb[j].  The block absmax, E8M0 code and converts are those
+// of mx_quantize_quad_bf16, so codes and scale are bit-identical to it.
+// Returns the 16 code bytes (element 2j in the low nibble of byte j).
+__device__ __forceinline__ u32x4 mx_quantize_lane_bf16(const bf16x8 (&xb)[4], unsigned* code) {
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const u32x4 v = __builtin_bit_cast(u32x4, xb[j]);
+    m = bf16x2_absmax_bits(m, bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w)));
+  }
+  m = max(m & 0xFFFFu, m >> 16);
+  const unsigned c = e8m0_code_from_expfield(m >> 7);
+  const float scale = e8m0_as_scale(c);
+  unsigned o[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    unsigned out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[j][0], xb[j][1]}, scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[j][2], xb[j][3]}, scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[j][4], xb[j][5]}, scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, (bf16x2){xb[j][6], xb[j][7]}, scale, 3);
+    o[j] = out;
+  }
+  *code = c;
+  return (u32x4){o[0], o[1], o[2], o[3]};
+}
+
 }  // namespace mxq

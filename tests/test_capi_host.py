@@ -164,6 +164,22 @@ def test_transfp4_validation(lib):
     assert d(NULL, NULL, NULL, NULL, NULL, 0, 64, NULL, 0, NULL) == SUCCESS
 
 
+def test_w4a4_dynamic_validation(lib):
+    f = lib.mxq_gemm_w4a4_dynamic
+    assert f(A16, A16b, A16c, 17, 8, 512, A16d, 1, NULL) == INVALID  # m > 16
+    assert f(A16, A16b, A16c, 17, 8, 0, A16d, 1, NULL) == INVALID
+    assert f(A16, A16b, A16c, 4, 8, 544, A16d, 1, NULL) == INVALID  # k % 512
+    assert f(A16, A16b, A16c, 4, 8, 1 << 25, A16d, 1, NULL) == INVALID  # k > 2^24
+    assert f(A16, A16b, A16c, -1, 8, 512, A16d, 1, NULL) == INVALID
+    assert f(A16, A16b, A16c, 4, 8, 512, A16d, 5, NULL) == INVALID  # dtype
+    assert f(NULL, A16b, A16c, 4, 8, 512, A16d, 1, NULL) == INVALID  # x missing
+    assert f(A16, A16b, A16c, 4, 8, 512, NULL, 1, NULL) == INVALID  # c missing
+    assert f(MIS, A16b, A16c, 4, 8, 512, A16d, 1, NULL) == MISALIGNED
+    assert f(A16, A16b, MIS, 4, 8, 512, A16d, 1, NULL) == MISALIGNED
+    assert f(NULL, NULL, NULL, 0, 8, 512, NULL, 1, NULL) == SUCCESS  # empty: no-op
+    assert f(NULL, NULL, NULL, 4, 0, 512, NULL, 1, NULL) == SUCCESS
+
+
 def test_no_device_reports_not_supported(lib):
     """Valid arguments on a machine without a GPU: NOT_SUPPORTED, no launch."""
     import torch
@@ -173,6 +189,7 @@ def test_no_device_reports_not_supported(lib):
     assert lib.mxq_quantize(A16, 1, 4, 32, A16b, A16c, NULL) == NOT_SUPPORTED
     assert lib.mxq_quantize_hadamard(A16, 1, 4, 32, 32, A16b, A16c, NULL) == NOT_SUPPORTED
     assert lib.mxq_gemm_w4a4(A16, A16b, A16c, A16d, 4, 4, 32, A16, 1, NULL) == NOT_SUPPORTED
+    assert lib.mxq_gemm_w4a4_dynamic(A16, A16b, A16c, 4, 4, 512, A16d, 1, NULL) == NOT_SUPPORTED
     assert lib.nvq_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, NULL) == NOT_SUPPORTED
     assert lib.mxq_transfp4_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, A16, A16b, NULL) == NOT_SUPPORTED
 

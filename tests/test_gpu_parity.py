@@ -773,6 +773,76 @@ def test_w4a8_skinny_full_size_sampled(m):
     say(f"w4a8 skinny m={m}: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
 
 
+def same_bits(a, b):
+    return a.dtype == b.dtype and a.shape == b.shape and torch.equal(a.view(torch.int16 if a.element_size() == 2
+                                                                              else torch.int32),
+                                                                       b.view(torch.int16 if b.element_size() == 2
+                                                                              else torch.int32))
+
+
+# W4A4 from bf16 activations quantized in the kernel (the GEMM prologue):
+# bit-identical to quantize-then-GEMM, and within the product bound of the
+# oracle.  m <= 16, ragged n over the 112-row blocks, odd and even stage
+# counts, more than eight blocks (several k rotations).
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 512), (5, 2000, 1536), (16, 1800, 4096), (11, 1121, 2048),
+                                   (16, 250, 1024), (3, 2500, 1024), (8, 999, 3072), (2, 7, 512), (16, 3000, 5120)])
+def test_w4a4_dynamic_equals_quantize_then_gemm(m, n, k):
+    rng = np.random.default_rng(3 * m + n + 7 * k)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * np.exp2(rng.integers(-8, 9, size=(m, 1))))
+                               .astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    qb, sb = assert_mx_codes(w, f"dyn W {n}x{k}")
+    xd, qbd, sbd = dev(x), dev(qb), dev(sb)
+    qa, sa = mxq.quantize(xd)
+    for dt in (torch.float32, torch.bfloat16):
+        c = mxq.gemm_w4a4_dynamic(xd, qbd, sbd, dt)
+        ref = mxq.gemm_w4a4(qa, sa, qbd, sbd, dt)
+        assert same_bits(c, ref), f"dynamic {m}x{n}x{k} {dt}: differs from quantize + gemm"
+    qo, so = oracle.mx_quantize(x)
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qo, so), oracle.mx_dequantize(qb, sb))
+    check_product(host(c), yref, S, True, f"dynamic {m}x{n}x{k} vs oracle")
+
+
+def test_w4a4_dynamic_edge_activations():
+    """Zero, tiny, subnormal, huge and tied activation values: the in-kernel
+    quantizer must give what mxq_quantize gives, bit for bit."""
+    m, n, k = 16, 300, 1024
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, ::3] = 2.0 ** -133
+    x[3] = 2.0 ** -126 * rng.integers(-3, 4, size=k)
+    x[4] = np.float32(3.0e38) * np.sign(rng.standard_normal(k))
+    x[5] = 0.25 * rng.integers(-24, 25, size=k)  # many E2M1 ties
+    x[6, :32] = [0.0625, 0.375, 0.078125, 0.25] + [0.0] * 28
+    xb = synth.f32_to_bf16_bits(x)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 2).astype(np.float32))
+    qb, sb = mxq.quantize(dev(w))
+    qa, sa = mxq.quantize(dev(xb))
+    for dt in (torch.float32, torch.bfloat16):
+        c = mxq.gemm_w4a4_dynamic(dev(xb), qb, sb, dt)
+        assert same_bits(c, mxq.gemm_w4a4(qa, sa, qb, sb, dt)), f"edge activations {dt}"
+
+
+def test_w4a4_dynamic_full_size():
+    """The 28672 x 8192 decode weight, 16 bf16 activation rows: the whole
+    output equals quantize + gemm, sampled columns against the oracle."""
+    _, qo, so = decode_weight()
+    _, x = synth.decode_gemv(16)
+    xd, qd, sd = dev(x), dev(qo), dev(so)
+    c = mxq.gemm_w4a4_dynamic(xd, qd, sd, torch.bfloat16)
+    qa, sa = mxq.quantize(xd)
+    assert same_bits(c, mxq.gemm_w4a4(qa, sa, qd, sd, torch.bfloat16)), "full size: differs from quantize + gemm"
+    n = qo.shape[0]
+    rng = np.random.default_rng(500)
+    cols = np.unique(np.concatenate([rng.choice(n, size=256, replace=False), [0, n - 1]]))
+    qx, sx = oracle.mx_quantize(x)
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qx, sx), oracle.mx_dequantize(qo[cols], so[cols]))
+    worst = check_product(host(c)[:, cols], yref, S, True, "dynamic 16x28672x8192")
+    say(f"w4a4 dynamic m=16: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
+
+
 def test_w4a4_all_16x16_code_products_exact():
     """C[i][j] = E2M1(i) * E2M1(j) through the block-scaled MFMA (unit scales)."""
     k = 64
