@@ -9,7 +9,9 @@ already resident in HBM:
          with the 32-point block Hadamard rotation fused ahead of it; the
          TransFP4 block quantize (rotation, bf16 residual, NVFP4/INT4 choice)
          of the same tensor and its dequantization
-  gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
+  gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16;
+         on the same weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x) and
+         W4A4 from bf16 x quantized inside the GEMM (the small-m kernel)
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
          (bf16 output, and MXFP4 output quantized in the epilogue); MXFP8
          quantize of the same A + W4A8 GEMM 8192^3 (E4M3 x E2M1 MFMA)
@@ -177,6 +179,23 @@ def main():
             ops.append((f"gemv_w4a16_m{m}",
                         rotating([(q, s, xm, ym) for q, s in copies], lambda q, s, x, y: mxq.gemv_w4a16(q, s, x, y=y)),
                         gemv_bytes(n2, k2, m), 2 * m * n2 * k2))
+        # decode-sized W4A4 / W4A8 on the same weight (the small-m kernel:
+        # the weight stream bounds it), and W4A4 straight from bf16
+        # activations with their quantization fused into the GEMM
+        x16 = to_dev(synth.decode_gemv(16)[1])
+        qx16, sx16 = mxq.quantize(x16)
+        qx8, sx8 = mxq.quantize_fp8(x16)
+        y16 = torch.empty((16, n2), dtype=bf16, device=dev)
+        out16 = 16 * n2 * 2
+        ops.append(("decode_w4a4_m16", rotating([(q, s) for q, s in copies],
+                                                lambda q, s: mxq.gemm_w4a4(qx16, sx16, q, s, c=y16)),
+                    mx_bytes(n2, k2) + mx_bytes(16, k2) + out16, 2 * 16 * n2 * k2))
+        ops.append(("decode_w4a8_m16", rotating([(q, s) for q, s in copies],
+                                                lambda q, s: mxq.gemm_w4a8(qx8, sx8, q, s, c=y16)),
+                    mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2))
+        ops.append(("decode_w4a4_dynamic_m16", rotating([(q, s) for q, s in copies],
+                                                        lambda q, s: mxq.gemm_w4a4_dynamic(x16, q, s, c=y16)),
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2))
     if "w4a4" in parts:
         a4, b4 = synth.w4a4_operands()
         a4d = to_dev(a4)
@@ -377,7 +396,8 @@ def _src_digest(files):
 
 
 KERNEL_SOURCES = {"gemv": ["w4a16.hip", "mxq_device.h"], "w4a4": ["w4a4.hip", "mxq_device.h", "mxq_gemm_common.h"],
-                  "w4a8": ["w4a8.hip", "mxq_device.h", "mxq_gemm_common.h"], "quantize": ["quant.hip", "mxq_device.h"]}
+                  "w4a8": ["w4a8.hip", "mxq_device.h", "mxq_gemm_common.h"], "quantize": ["quant.hip", "mxq_device.h"],
+                  "skinny": ["gemm_skinny.hip", "mxq_device.h", "mxq_gemm_common.h"]}
 
 
 def traffic_for(name):
