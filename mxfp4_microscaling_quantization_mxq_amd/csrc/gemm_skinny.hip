@@ -7,8 +7,9 @@
 // rows as on 256, and a 28672-row weight gives it only 112 tiles for 256
 // CUs; measured, the W4A4 and W4A8 tile kernels took 53-69 us at every
 // m <= 256 on a 28672 x 8192 MXFP4 weight, against about 21 us for the
-// weight read itself.  Batch size picks the kernel [deployment guide,
-// sec. 5.2: small batches and large batches take different GEMM kernels].
+// weight read itself.  Batch size picks the kernel ["FP4 quantization
+// analysis" page, sec. 5.2: small batches and large ones use different GEMM
+// back ends].
 //
 // Instruction: V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the activations as
 // operand A (E2M1 or E4M3) and the weights as operand B (E2M1).  Lane l
