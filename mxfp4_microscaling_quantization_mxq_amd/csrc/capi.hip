@@ -190,7 +190,7 @@ mxq_status mxq_gemm_w4a4_dynamic(const void* x, const uint8_t* bq, const uint8_t
                                  int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
   if (m < 0 || n < 0 || k < 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
   if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if (!mxq::w4a4_dynamic_applies(m, k) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (m > 16 || k % 512 != 0 || k > (1 << 24) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
   if (!c) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
   if (k == 0) {

@@ -531,7 +531,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16
 bool gemm_skinny_applies(int64_t m, int64_t k) {
   // 32-bit copy offsets: a weight panel of at most 224 rows and a 128-row
   // activation panel stay below 2^31 bytes for k <= 2^24
-  return m >= 1 && m <= 128 && k % 512 == 0 && k <= (1 << 24);
+  return m >= 1 && m <= 128 && k >= 512 && k % 512 == 0 && k <= (1 << 24);
 }
 
 hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
@@ -577,8 +577,6 @@ static void launch_skd(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, 
 // at m = 16, but 33.5 vs 27.2 us at m = 32 and 50.6 vs 29.9 us at m = 64,
 // where every block pulls a bf16 tile (4x the bytes of its codes) through
 // the same copy path as the weights.
-bool w4a4_dynamic_applies(int64_t m, int64_t k) { return m <= 16 && gemm_skinny_applies(m, k); }
-
 hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                int64_t k, void* c, bool bf16_out, hipStream_t st) {
   launch_skd<16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);

@@ -70,8 +70,10 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
 }
 // The same 16-byte copy through a buffer resource (buffer_load_dwordx4 ...
 // lds): base and size in SGPRs, a 32-bit per-lane offset and a uniform
-// offset.  Measured about 3 % faster than the 64-bit-address form in the
-// block-scaled GEMM rings.
+// offset; reads past the size return zero.  Measured about 3 % faster than
+// the 64-bit-address form in the block-scaled GEMM rings.  The compiler
+// tracks it as a plain vector-memory load, not as an LDS write: the kernels
+// wait for it with explicit vmcnt counts before a barrier.
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);

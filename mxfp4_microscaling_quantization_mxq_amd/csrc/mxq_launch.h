@@ -51,9 +51,8 @@ hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_
 hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
                               int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st);
 // W4A4 with bf16 activations x[m][k] quantized to MXFP4 inside the kernel:
-// bit-identical to launch_mx_quantize followed by launch_w4a4.  Applies
-// where w4a4_dynamic_applies: m <= 16 and gemm_skinny_applies.
-bool w4a4_dynamic_applies(int64_t m, int64_t k);
+// bit-identical to launch_mx_quantize followed by launch_w4a4.  For
+// 1 <= m <= 16 where gemm_skinny_applies.
 hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                int64_t k, void* c, bool bf16_out, hipStream_t st);
 

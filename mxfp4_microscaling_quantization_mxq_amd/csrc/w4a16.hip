@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "mxq_device.h"
+#include "mxq_gemm_common.h"
 #include "mxq_launch.h"
 
 namespace mxq {
@@ -452,31 +453,6 @@ __global__ __launch_bounds__(256) void k_w4a16_decode_mfma(const uint8_t* __rest
 // The NVFP4 tensor scale multiplies the fp32 result in the epilogue.
 constexpr int kGBM = 256, kGBN = 256, kGRing = 3;
 constexpr int kGXStage = kGBM * 128, kGWStage = kGBN * 32;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void gdma16(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
-}
-// The same copy through a buffer resource (buffer_load_dwordx4 ... lds):
-// base and record count in SGPRs, a 32-bit per-lane offset and a uniform
-// per-stage offset.  The compiler tracks it as a plain vector-memory
-// operation, so LDS reads of other slots that follow it need not drain it.
-constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
-}
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
-}
-__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
-}
-template <int N>
-__device__ __forceinline__ void gwait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // One ring slot of the GEMM (activations and weight codes of one stage).
 // Every slot is its own LDS variable and is addressed only through
 // compile-time slot indices, so the compiler can tell that the reads of one
@@ -531,8 +507,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
   // in the free slot and is never read)
   // buffer resources of the tile's row panels; per-lane offsets fixed for
   // the whole k loop, the stage moves the uniform offset only
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const uint8_t*)x + m0 * kx, (unsigned)(rows_x * kx));
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * kq, (unsigned)(rows_w * kq));
+  const __amdgpu_buffer_rsrc_t rx = panel_rsrc((const uint8_t*)x + m0 * kx, rows_x * kx);
+  const __amdgpu_buffer_rsrc_t rw = panel_rsrc(wq + n0 * kq, rows_w * kq);
   unsigned offx[CJX], offw[CJW];
 #pragma unroll
   for (int j = 0; j < CJX; j++) {
@@ -657,7 +633,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
     __builtin_amdgcn_sched_barrier(0);
     load_scales(min(s + 1, nstages - 1), sc_nxt);
     __builtin_amdgcn_sched_barrier(0);
-    gwait_vmcnt<CJX + CJW + JB>();
+    wait_vmcnt<CJX + CJW + JB>();
     __builtin_amdgcn_s_barrier();  // no fence: the prefetched stages stay in flight
     __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, (B + kGRing - 1) % kGRing>{}, min(s + kGRing - 1, nstages - 1));
@@ -680,7 +656,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
   }
   if (s < nstages) step(std::integral_constant<int, 0>{}, s);
   if (s + 1 < nstages) step(std::integral_constant<int, 1>{}, s + 1);
-  gwait_vmcnt<0>();
+  wait_vmcnt<0>();
 
   const float st = kNv ? *gscale : 1.0f;
   if constexpr (kBf16Out) {
@@ -822,9 +798,6 @@ constexpr int kDdRowB = kDdK / 2;     // code bytes per row per stage
 constexpr int kDdScB = kDdK / 32;     // scale bytes per row per stage
 constexpr int kDdXRowB = kDdK * 2;    // activation bytes per row per stage
 
-__device__ __forceinline__ void gdma4(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
-}
 
 // One ring slot: codes, activations and scales of one stage.  Every slot is
 // its own LDS variable and every slot index below is a compile-time
@@ -894,9 +867,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   }
   // buffer resources over the block's weight, scale and activation panels
   // (32-bit lane offsets; the panels stay below 2^31 bytes for k <= 2^24)
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wq + n0 * kq, (unsigned)(rows_w * kq));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(ws + n0 * ks, (unsigned)(rows_w * ks));
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (unsigned)(m * kx));
+  const __amdgpu_buffer_rsrc_t rw = panel_rsrc(wq + n0 * kq, rows_w * kq);
+  const __amdgpu_buffer_rsrc_t rs = panel_rsrc(ws + n0 * ks, rows_w * ks);
+  const __amdgpu_buffer_rsrc_t rx = panel_rsrc(x, m * kx);
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
     DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
@@ -969,7 +942,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     if (NR > 3) step(I3{}, s + 2);
     step(I0{}, s + NR - 1);
   }
-  gwait_vmcnt<0>();
+  wait_vmcnt<0>();
 
   // lane holds y[4g + i][n0 + wrow]
   const int64_t nn = n0 + wrow;

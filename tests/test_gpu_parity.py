@@ -925,6 +925,53 @@ def test_w4a4_quant_full_size_and_empty_k():
     assert torch.count_nonzero(cq0).item() == 0 and torch.count_nonzero(cs0).item() == 0
 
 
+# Long k (2^20 = 1,048,576, 2048 stages of 512): the products' 32-bit copy
+# offsets, k rotations and stage loops far from the small test shapes.
+# Random codes and scales stand in for quantized tensors (host memory stays
+# small); outputs are checked on sampled rows and columns.
+@pytest.mark.parametrize("kind,m,n,k", [("w4a4", 16, 130, 1 << 20), ("w4a4", 260, 300, 1 << 20),
+                                        ("w4a4", 40, 70, (1 << 20) + 32), ("w4a8", 16, 130, 1 << 20),
+                                        ("w4a8", 260, 300, 1 << 20), ("w4a8", 40, 70, (1 << 20) + 32),
+                                        ("gemv", 1, 7, 1 << 20), ("gemv", 3, 300, 1 << 20),
+                                        ("dyn", 16, 130, 1 << 20)])
+def test_products_long_k(kind, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    qb = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    sb = rng.integers(118, 136, size=(n, k // 32), dtype=np.uint8)
+    rows = np.arange(m) if m <= 16 else np.unique(np.concatenate([rng.choice(m, 4, replace=False), [0, m - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(n, 4, replace=False), [0, n - 1]]))
+    bd = oracle.mx_dequantize(qb[cols], sb[cols])
+    extra = None
+    if kind in ("w4a4", "w4a8"):
+        sa = rng.integers(118, 136, size=(m, k // 32), dtype=np.uint8)
+        if kind == "w4a4":
+            qa = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+            c = host(mxq.gemm_w4a4(dev(qa), dev(sa), dev(qb), dev(sb), torch.float32))
+            ad = oracle.mx_dequantize(qa[rows], sa[rows])
+        else:
+            qa = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+            qa[(qa & 0x7F) == 0x7F] ^= 1  # no NaN codes
+            c = host(mxq.gemm_w4a8(dev(qa), dev(sa), dev(qb), dev(sb), torch.float32))
+            ad = oracle.mx8_dequantize(qa[rows], sa[rows])
+            extra = w4a8_block_sum_allowance(qa[rows], sa[rows], qb[cols], sb[cols])
+    else:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        if kind == "gemv":
+            c = host(mxq.gemv_w4a16(dev(qb), dev(sb), dev(x), torch.float32))
+            ad = oracle.to_f64(x[rows])
+        else:
+            xd, qbd, sbd = dev(x), dev(qb), dev(sb)
+            cd = mxq.gemm_w4a4_dynamic(xd, qbd, sbd, torch.float32)
+            qa_d, sa_d = mxq.quantize(xd)
+            assert same_bits(cd, mxq.gemm_w4a4(qa_d, sa_d, qbd, sbd, torch.float32)), "long k: dynamic"
+            c = host(cd)
+            qx, sx = oracle.mx_quantize(x[rows])
+            ad = oracle.mx_dequantize(qx, sx)
+    yref, S = oracle.gemm_nt(ad, bd)
+    worst = check_product(c[np.ix_(rows, cols)], yref, S, False, f"{kind} {m}x{n}x{k}", extra)
+    say(f"{kind} {m}x{n}x{k}: worst |err|/S {worst:.3g}")
+
+
 def test_products_with_empty_k_write_zeros():
     y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
     e = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
