@@ -229,6 +229,25 @@ MXQ_API mxq_status mxq_gemm_w4a4_dynamic(const void *x, const uint8_t *bq,
                                  hipStream_t stream);
 
 /*
+ * W4A8 product from bf16 activations quantized to MXFP8 inside the kernel:
+ * c[m][n] = sum_k MXFP8(x)[m][k] * B_hat[n][k], where MXFP8(x) is exactly
+ * what mxq_quantize_fp8 writes for x, so c is bit-identical to
+ * mxq_quantize_fp8 followed by mxq_gemm_w4a8 (whose accuracy note applies).
+ * [MXFP8 activations with a dynamic per-token-block quantization: infra-
+ * guide sec. 4.2 (mxfp8); TransFP4 page sec. 2.5: conversion in the GEMM's
+ * load stage.]  x bf16 [m][k]; B = (bq[n][k/2], bs[n][k/32]); c written as
+ * cdt.  For decode-sized batches, as mxq_gemm_w4a4_dynamic: 1 <= m <= 16,
+ * k % 512 == 0, k <= 2^24, else MXQ_ERROR_INVALID_VALUE (larger batches:
+ * mxq_quantize_fp8 once, then mxq_gemm_w4a8, which is faster there).  m ==
+ * 0 or n == 0: no-op; k == 0 writes zeros.  Errors otherwise as
+ * mxq_gemm_w4a4.
+ */
+MXQ_API mxq_status mxq_gemm_w4a8_dynamic(const void *x, const uint8_t *bq,
+                                 const uint8_t *bs, int64_t m, int64_t n,
+                                 int64_t k, void *c, mxq_dtype cdt,
+                                 hipStream_t stream);
+
+/*
  * NVFP4 quantize.  x[rows][k] (xdt) -> q[rows][k/2] packed E2M1 codes,
  * s[rows][k/16] E4M3 block-scale codes, and the fp32 tensor scale *gscale
  * (a single float in device memory, the dequantization multiplier).

@@ -34,7 +34,7 @@ STATUS = {
 API = (
     "mxq_status_string", "mxq_version", "mxq_quantize", "mxq_quantize_hadamard", "mxq_quantize_fp8",
     "mxq_dequantize", "mxq_gemv_w4a16", "mxq_gemm_w4a4", "mxq_gemm_w4a4_quant", "mxq_gemm_w4a4_dynamic",
-    "mxq_gemm_w4a8", "nvq_quantize", "nvq_dequantize", "nvq_gemm", "mxq_transfp4_quantize", "mxq_transfp4_dequantize",
+    "mxq_gemm_w4a8", "mxq_gemm_w4a8_dynamic", "nvq_quantize", "nvq_dequantize", "nvq_gemm", "mxq_transfp4_quantize", "mxq_transfp4_dequantize",
 )
 
 
@@ -72,6 +72,7 @@ def capi() -> ctypes.CDLL:
     lib.mxq_gemm_w4a4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
     lib.mxq_gemm_w4a4_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
     lib.mxq_gemm_w4a4_dynamic.argtypes = [P, P, P, I64, I64, I64, P, I, P]
+    lib.mxq_gemm_w4a8_dynamic.argtypes = [P, P, P, I64, I64, I64, P, I, P]
     lib.nvq_quantize.argtypes = [P, I, I64, I64, P, I, P, P, P]
     lib.nvq_dequantize.argtypes = [P, P, P, I64, I64, P, I, P]
     lib.nvq_gemm.argtypes = [P, P, P, I64, I64, P, I64, P, I, P]
@@ -220,10 +221,7 @@ def gemm_w4a4(aq, as_, bq, bs, out_dtype=None, c=None):
     return c
 
 
-def gemm_w4a4_dynamic(x, bq, bs, out_dtype=None, c=None):
-    """c[m, n] = MXFP4(x)[m, k] @ deq(B)[n, k]^T with bf16 x quantized inside
-    the kernel (bit-identical to gemm_w4a4(*quantize(x), bq, bs)); m <= 16,
-    k % 512 == 0."""
+def _gemm_dynamic(entry, x, bq, bs, out_dtype, c):
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
     _need(x, "x", torch.bfloat16)
@@ -235,9 +233,22 @@ def gemm_w4a4_dynamic(x, bq, bs, out_dtype=None, c=None):
         raise ValueError("x and B disagree on k")
     if c is None:
         c = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    _check(capi().mxq_gemm_w4a4_dynamic(_p(x), _p(bq), _p(bs), m, n, k, _p(c), _dtype_code(c.dtype), _stream()),
-           "mxq_gemm_w4a4_dynamic")
+    _check(getattr(capi(), entry)(_p(x), _p(bq), _p(bs), m, n, k, _p(c), _dtype_code(c.dtype), _stream()), entry)
     return c
+
+
+def gemm_w4a4_dynamic(x, bq, bs, out_dtype=None, c=None):
+    """c[m, n] = MXFP4(x)[m, k] @ deq(B)[n, k]^T with bf16 x quantized inside
+    the kernel (bit-identical to gemm_w4a4(*quantize(x), bq, bs)); m <= 16,
+    k % 512 == 0."""
+    return _gemm_dynamic("mxq_gemm_w4a4_dynamic", x, bq, bs, out_dtype, c)
+
+
+def gemm_w4a8_dynamic(x, bq, bs, out_dtype=None, c=None):
+    """c[m, n] = MXFP8(x)[m, k] @ deq(B)[n, k]^T with bf16 x quantized to MXFP8
+    inside the kernel (bit-identical to gemm_w4a8(*quantize_fp8(x), bq, bs));
+    m <= 16, k % 512 == 0."""
+    return _gemm_dynamic("mxq_gemm_w4a8_dynamic", x, bq, bs, out_dtype, c)
 
 
 def gemm_w4a8(aq8, as_, bq, bs, out_dtype=None, c=None):

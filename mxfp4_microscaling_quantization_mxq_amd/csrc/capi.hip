@@ -205,6 +205,25 @@ mxq_status mxq_gemm_w4a4_dynamic(const void* x, const uint8_t* bq, const uint8_t
   return launched(mxq::launch_w4a4_dynamic((const uint16_t*)x, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
 }
 
+mxq_status mxq_gemm_w4a8_dynamic(const void* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
+                                 int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return MXQ_SUCCESS;
+  if (m > 16 || k % 512 != 0 || k > (1 << 24) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (!c) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
+  if (k == 0) {
+    mxq_status d = check_device();
+    if (d != MXQ_SUCCESS) return d;
+    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
+  }
+  if (!x || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_w4a8_dynamic((const uint16_t*)x, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
+}
+
 mxq_status mxq_gemm_w4a4_quant(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                                int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t stream) {
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || n % 32 != 0) return MXQ_ERROR_INVALID_VALUE;

@@ -296,20 +296,23 @@ static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, c
 }
 
 // ---------------------------------------------------------------------------
-// W4A4 with the activations quantized in the kernel (MXFP4 of bf16 x, the
-// quantizer of mxq_quantize): the bf16 activation rows of a stage ride in
-// the ring instead of codes, and the block quantizes them once per stage
-// into a single MXFP4 tile that the MFMAs then read exactly as above.
+// W4A4 / W4A8 with the activations quantized in the kernel (MXFP4 or MXFP8
+// of bf16 x, with the quantizers of mxq_quantize / mxq_quantize_fp8): the
+// bf16 activation rows of a stage ride in the ring instead of codes, and
+// the block quantizes them once per stage into a single tile that the MFMAs
+// then read exactly as above.
 //   * After the stage barrier and the refill copies, lane q of the block
 //     takes MX blocks q, q + 64 NW, ... of the stage (one whole 32-element
-//     block per lane: mx_quantize_lane_bf16), writes its 16 code bytes and
-//     E8M0 byte into the tile, and a second barrier publishes the tile.
+//     block per lane: mx_quantize_lane_bf16 / mx8_quantize_lane_bf16),
+//     writes its 16 or 32 code bytes and its E8M0 byte into the tile, and a
+//     second barrier publishes the tile.
 //   * The tile is single: the next stage's quantization starts after the
 //     next stage barrier, which every wave reaches only once its reads of
 //     the tile are complete.
 //   * Blocks of 112 weight rows and the k order of skinny_rotation, as in
-//     the W4A4 kernel for the same m: the product is bit-identical to
-//     mxq_quantize followed by mxq_gemm_w4a4.
+//     the kernel above for the same m: the product is bit-identical to
+//     quantize-then-GEMM (mxq_quantize + mxq_gemm_w4a4, or
+//     mxq_quantize_fp8 + mxq_gemm_w4a8).
 template <int MT, int NW, int KS>
 struct SkDynSlot {
   using G = SkGeom<KS, false>;
@@ -324,23 +327,25 @@ __device__ __forceinline__ SkDynSlot<MT, NW, KS>& sk_dyn_slot() {
   __shared__ __attribute__((aligned(1024))) SkDynSlot<MT, NW, KS> slot;
   return slot;
 }
-template <int MT, int KS>
+template <int MT, int KS, bool kFp8>
 struct SkDynTile {
-  uint8_t x[MT * KS / 2];      // MXFP4 codes, unit b of row r at slot b ^ (r % 16)
+  // codes in the layout of the activation slot above: unit v of row r at
+  // slot v ^ (r % swz(units per row))
+  uint8_t x[MT * SkGeom<KS, kFp8>::XRowB];
   uint8_t xs[MT / 16 * 256];   // E8M0 codes, a 256-byte region per 16 rows
 };
-template <int MT, int KS>
-__device__ __forceinline__ SkDynTile<MT, KS>& sk_dyn_tile() {
-  __shared__ __attribute__((aligned(1024))) SkDynTile<MT, KS> tile;
+template <int MT, int KS, bool kFp8>
+__device__ __forceinline__ SkDynTile<MT, KS, kFp8>& sk_dyn_tile() {
+  __shared__ __attribute__((aligned(1024))) SkDynTile<MT, KS, kFp8> tile;
   return tile;
 }
 
-template <int MT, int NW, int NR, int KS, bool kBf16Out>
-__global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16_t* __restrict__ x,
-                                                                   const uint8_t* __restrict__ bq,
-                                                                   const uint8_t* __restrict__ bs, int64_t m,
-                                                                   int64_t n, int64_t k, void* __restrict__ c) {
-  using G = SkGeom<KS, false>;
+template <bool kFp8, int MT, int NW, int NR, int KS, bool kBf16Out>
+__global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* __restrict__ x,
+                                                              const uint8_t* __restrict__ bq,
+                                                              const uint8_t* __restrict__ bs, int64_t m,
+                                                              int64_t n, int64_t k, void* __restrict__ c) {
+  using G = SkGeom<KS, kFp8>;
   using Slot = SkDynSlot<MT, NW, KS>;
   constexpr int RB = 16 * NW;                         // weight rows per block
   constexpr int MTT = MT / 16;                        // 16-row activation tiles
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16
   constexpr int BPR = KS / 32;                        // MX blocks per row per stage
   constexpr int NB = MT * BPR;                        // MX blocks per stage
   constexpr int QPL = (NB + 64 * NW - 1) / (64 * NW); // blocks each lane quantizes
-  constexpr int WSW = swz(G::U);
+  constexpr int WSW = swz(G::U), TSW = swz(G::XU);
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * Slot::XRowB, sl.x + dx[j]);
   };
 
-  SkDynTile<MT, KS>& tile = sk_dyn_tile<MT, KS>();
+  SkDynTile<MT, KS, kFp8>& tile = sk_dyn_tile<MT, KS, kFp8>();
   auto quantize = [&](auto slot_tag) {
     constexpr int B = decltype(slot_tag)::value;
     const Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
@@ -408,8 +413,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16
 #pragma unroll
         for (int u = 0; u < 4; u++) xb[u] = *(const bf16x8*)(sl.x + r * Slot::XRowB + (4 * b + u) * 16);
         unsigned code;
-        const u32x4 codes = mx_quantize_lane_bf16(xb, &code);
-        *(u32x4*)(tile.x + r * G::RowB + ((b ^ (r % WSW)) << 4)) = codes;
+        uint8_t* trow = tile.x + r * G::XRowB;
+        if constexpr (kFp8) {
+          u32x2 cb[4];
+          mx8_quantize_lane_bf16(xb, &code, cb);
+          *(u32x4*)(trow + (((2 * b) ^ (r % TSW)) << 4)) = (u32x4){cb[0].x, cb[0].y, cb[1].x, cb[1].y};
+          *(u32x4*)(trow + (((2 * b + 1) ^ (r % TSW)) << 4)) = (u32x4){cb[2].x, cb[2].y, cb[3].x, cb[3].y};
+        } else {
+          *(u32x4*)(trow + ((b ^ (r % TSW)) << 4)) = mx_quantize_lane_bf16(xb, &code);
+        }
         tile.xs[(r / 16) * 256 + (r % 16) * G::ScB + b] = (uint8_t)code;
       }
     }
@@ -443,10 +455,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a4_dynamic_skinny(const uint16
       const int sw = (int)((wss[i] >> (8 * g)) & 0xFFu);
 #pragma unroll
       for (int t = 0; t < MTT; t++) {
-        const u32x4 cx = *(const u32x4*)(tile.x + (16 * t + col) * G::RowB + slot);
-        const i32x8 xf = {(int)cx.x, (int)cx.y, (int)cx.z, (int)cx.w, 0, 0, 0, 0};
+        const uint8_t* xr = tile.x + (16 * t + col) * G::XRowB;
+        i32x8 xf;
+        if constexpr (kFp8) {
+          const u32x4 lo = *(const u32x4*)(xr + (((8 * i + g) ^ (col % TSW)) << 4));
+          const u32x4 hi = *(const u32x4*)(xr + (((8 * i + 4 + g) ^ (col % TSW)) << 4));
+          xf = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+          const u32x4 cx = *(const u32x4*)(xr + (((4 * i + g) ^ (col % TSW)) << 4));
+          xf = (i32x8){(int)cx.x, (int)cx.y, (int)cx.z, (int)cx.w, 0, 0, 0, 0};
+        }
         const int sx = (int)((xss[t][i] >> (8 * g)) & 0xFFu);
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf, acc[t], kFmtFp4, kFmtFp4, 0, sx, 0, sw);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf, acc[t], kFp8 ? kFmtFp8 : kFmtFp4, kFmtFp4,
+                                                                  0, sx, 0, sw);
       }
     }
   };
@@ -560,26 +581,34 @@ hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8
   return hipGetLastError();
 }
 
-template <int MT, int NW, int NR, int KS>
+template <bool kFp8, int MT, int NW, int NR, int KS>
 static void launch_skd(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n, int64_t k,
                        void* c, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a4_dynamic_skinny<MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
+    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
                        k, c);
   else
-    hipLaunchKernelGGL((k_w4a4_dynamic_skinny<MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
-                       k, c);
+    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, x, bq, bs, m,
+                       n, k, c);
 }
 
 // Up to 16 activation rows.  Measured on a 28672 x 8192 weight against
-// mxq_quantize + the W4A4 kernel: 22.8 vs 24.5 us at m = 1, 25.0 vs 25.0 us
-// at m = 16, but 33.5 vs 27.2 us at m = 32 and 50.6 vs 29.9 us at m = 64,
-// where every block pulls a bf16 tile (4x the bytes of its codes) through
-// the same copy path as the weights.
+// quantize + the product kernel: W4A4 22.7 vs 24.5-24.8 us at m = 1,
+// 25.1-25.7 vs 24.9 us at m = 16, but 33.5 vs 27.2 us at m = 32 and 50.6 vs
+// 29.9 us at m = 64; W4A8 23.6 vs 25.1-25.5 us at m = 1, 26.4-27.6 vs 26.4 us
+// at m = 16, 38.6-42.0 vs 29.2-29.6 us at m = 32.  Every block pulls a
+// bf16 tile (4x the bytes of MXFP4 codes, 2x those of MXFP8) through the
+// same copy path as the weights.
 hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  launch_skd<16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
+  launch_skd<false, 16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
+                               int64_t k, void* c, bool bf16_out, hipStream_t st) {
+  launch_skd<true, 16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
   return hipGetLastError();
 }
 

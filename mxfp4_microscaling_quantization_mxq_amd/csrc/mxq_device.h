@@ -163,4 +163,57 @@ __device__ __forceinline__ u32x4 mx_quantize_lane_bf16(const bf16x8 (&xb)[4], un
   return (u32x4){o[0], o[1], o[2], o[3]};
 }
 
+// MXFP8 (E4M3 elements, E8M0 scale per 32) [infra-guide sec. 4.2, mxfp8;
+// sec. 1.2, E4M3 max 448].  Block code from the bf16 exponent field of the
+// block amax by the MXFP4 rule with E4M3's top exponent: max(ef - 8, 0), so
+// the largest magnitude scales into [256, 512).
+__device__ __forceinline__ unsigned e8m0_code_e4m3(unsigned ef) { return ef > 8u ? ef - 8u : 0u; }
+
+// E4M3 codes of 8 bf16 values under block code `code`: every magnitude is
+// clamped to 448 * 2^e first (the gfx950 scaled fp8 convert gives the NaN
+// code for scaled values past 448 instead of saturating; the clamp is exact:
+// 448 * 2^e is a bf16 value), then the scaled convert rounds to nearest
+// even.  Byte i of the result is element i.  Every MXFP8 quantizer of bf16
+// data in the library goes through this function.
+__device__ __forceinline__ u32x2 mx8_encode8_bf16(bf16x8 xb, unsigned code) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const float scale = e8m0_as_scale(code);
+  const unsigned lim = ((code + 8u) << 7) | 0x60u;  // bf16 bits of 448 * 2^e
+  const u16x2 lim2 = {(unsigned short)lim, (unsigned short)lim};
+  const u32x4 v = __builtin_bit_cast(u32x4, xb);
+  u32x4 cl;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const unsigned w = v[i];
+    const u16x2 mg = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+    cl[i] = __builtin_bit_cast(unsigned, __builtin_elementwise_min(mg, lim2)) | (w & 0x80008000u);
+  }
+  const bf16x8 xc = __builtin_bit_cast(bf16x8, cl);
+  s16x2 lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[0], xc[1]}, scale, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[2], xc[3]}, scale, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[4], xc[5]}, scale, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[6], xc[7]}, scale, true);
+  return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// Largest |x| of 8 bf16 values as bf16 magnitude bits.
+__device__ __forceinline__ unsigned bf16x8_absmax_bits(bf16x8 xb) {
+  const u32x4 v = __builtin_bit_cast(u32x4, xb);
+  const unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+// MXFP8 of one 32-element block held by one lane (elements 8j .. 8j+7 in
+// xb[j]): the block code and the 32 code bytes (element i in byte i).
+__device__ __forceinline__ void mx8_quantize_lane_bf16(const bf16x8 (&xb)[4], unsigned* code, u32x2 (&out)[4]) {
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) m = max(m, bf16x8_absmax_bits(xb[j]));
+  const unsigned c = e8m0_code_e4m3(m >> 7);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = mx8_encode8_bf16(xb[j], c);
+  *code = c;
+}
+
 }  // namespace mxq

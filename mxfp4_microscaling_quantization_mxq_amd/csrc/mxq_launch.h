@@ -55,6 +55,11 @@ hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8
 // 1 <= m <= 16 where gemm_skinny_applies.
 hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                int64_t k, void* c, bool bf16_out, hipStream_t st);
+// W4A8 with bf16 activations quantized to MXFP8 inside the kernel:
+// bit-identical to launch_mx8_quantize followed by launch_w4a8.  For
+// 1 <= m <= 16 where gemm_skinny_applies.
+hipError_t launch_w4a8_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
+                               int64_t k, void* c, bool bf16_out, hipStream_t st);
 
 // W4A4 with the product rounded to bf16 and quantized to MXFP4 along n in
 // the epilogue: cq[m][n/2], cs[m][n/32]; n % 32 == 0.

@@ -100,38 +100,16 @@ __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restric
 // One lane = 8 elements, a quad = one block; a lane stores 8 code bytes.
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ unsigned e8m0_code_e4m3(unsigned ef) { return ef > 8u ? ef - 8u : 0u; }
-
 __global__ __launch_bounds__(256) void k_mx8_quantize_bf16(const u32x4* __restrict__ x, u32x2* __restrict__ q,
                                                            uint8_t* __restrict__ s, int64_t nlanes) {
   int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nlanes) return;  // quads stay whole
   const bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
-  const u32x4 v = __builtin_bit_cast(u32x4, xb);
-  unsigned m = bf16x2_absmax_bits(bf16x2_absmax_bits(v.x, v.y), bf16x2_absmax_bits(v.z, v.w));
-  m = max(m & 0xFFFFu, m >> 16);
+  unsigned m = bf16x8_absmax_bits(xb);
   m = max(m, dpp_quad_xor1(m));
   m = max(m, dpp_quad_xor2(m));
   const unsigned code = e8m0_code_e4m3(m >> 7);
-  const float scale = e8m0_as_scale(code);
-  // |x| clamped to 448 * 2^e (bf16 bits: exponent field code + 8, mantissa
-  // .11), sign kept
-  const unsigned lim = ((code + 8u) << 7) | 0x60u;
-  const u16x2 lim2 = {(unsigned short)lim, (unsigned short)lim};
-  u32x4 cl;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const unsigned w = v[i];
-    const u16x2 mg = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
-    cl[i] = __builtin_bit_cast(unsigned, __builtin_elementwise_min(mg, lim2)) | (w & 0x80008000u);
-  }
-  const bf16x8 xc = __builtin_bit_cast(bf16x8, cl);
-  s16x2 lo = {0, 0}, hi = {0, 0};
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[0], xc[1]}, scale, false);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, (bf16x2){xc[2], xc[3]}, scale, true);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[4], xc[5]}, scale, false);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, (bf16x2){xc[6], xc[7]}, scale, true);
-  q[t] = (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  q[t] = mx8_encode8_bf16(xb, code);
   if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
 }
 

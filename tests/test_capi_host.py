@@ -180,6 +180,16 @@ def test_w4a4_dynamic_validation(lib):
     assert f(NULL, NULL, NULL, 4, 0, 512, NULL, 1, NULL) == SUCCESS
 
 
+def test_w4a8_dynamic_validation(lib):
+    f = lib.mxq_gemm_w4a8_dynamic
+    assert f(A16, A16b, A16c, 17, 8, 512, A16d, 1, NULL) == INVALID  # m > 16
+    assert f(A16, A16b, A16c, 4, 8, 544, A16d, 1, NULL) == INVALID  # k % 512
+    assert f(A16, A16b, A16c, 4, 8, 512, A16d, 5, NULL) == INVALID  # dtype
+    assert f(NULL, A16b, A16c, 4, 8, 512, A16d, 1, NULL) == INVALID  # x missing
+    assert f(A16, MIS, A16c, 4, 8, 512, A16d, 1, NULL) == MISALIGNED
+    assert f(NULL, NULL, NULL, 0, 8, 512, NULL, 1, NULL) == SUCCESS
+
+
 def test_no_device_reports_not_supported(lib):
     """Valid arguments on a machine without a GPU: NOT_SUPPORTED, no launch."""
     import torch
@@ -190,6 +200,7 @@ def test_no_device_reports_not_supported(lib):
     assert lib.mxq_quantize_hadamard(A16, 1, 4, 32, 32, A16b, A16c, NULL) == NOT_SUPPORTED
     assert lib.mxq_gemm_w4a4(A16, A16b, A16c, A16d, 4, 4, 32, A16, 1, NULL) == NOT_SUPPORTED
     assert lib.mxq_gemm_w4a4_dynamic(A16, A16b, A16c, 4, 4, 512, A16d, 1, NULL) == NOT_SUPPORTED
+    assert lib.mxq_gemm_w4a8_dynamic(A16, A16b, A16c, 4, 4, 512, A16d, 1, NULL) == NOT_SUPPORTED
     assert lib.nvq_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, NULL) == NOT_SUPPORTED
     assert lib.mxq_transfp4_quantize(A16, 1, 4, 32, A16b, 1, A16c, A16d, A16, A16b, NULL) == NOT_SUPPORTED
 

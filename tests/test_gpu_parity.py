@@ -825,6 +825,49 @@ def test_w4a4_dynamic_edge_activations():
         assert same_bits(c, mxq.gemm_w4a4(qa, sa, qb, sb, dt)), f"edge activations {dt}"
 
 
+# W4A8 from bf16 activations quantized to MXFP8 inside the GEMM: bit-identical
+# to quantize_fp8-then-GEMM (m <= 16), and within the W4A8 bound of the
+# oracle.
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 512), (5, 2000, 1536), (16, 1800, 4096), (13, 1121, 2048),
+                                   (16, 250, 1024), (2, 7, 512), (11, 3000, 5120), (9, 999, 3072)])
+def test_w4a8_dynamic_equals_quantize_then_gemm(m, n, k):
+    rng = np.random.default_rng(11 * m + n + 3 * k)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((m, k)) * np.exp2(rng.integers(-8, 9, size=(m, 1))))
+                               .astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    qb, sb = assert_mx_codes(w, f"dyn8 W {n}x{k}")
+    xd, qbd, sbd = dev(x), dev(qb), dev(sb)
+    qa, sa = mxq.quantize_fp8(xd)
+    for dt in (torch.float32, torch.bfloat16):
+        c = mxq.gemm_w4a8_dynamic(xd, qbd, sbd, dt)
+        ref = mxq.gemm_w4a8(qa, sa, qbd, sbd, dt)
+        assert same_bits(c, ref), f"dynamic w4a8 {m}x{n}x{k} {dt}: differs from quantize_fp8 + gemm"
+    qo, so = oracle.mx8_quantize(x)
+    yref, S = oracle.gemm_nt(oracle.mx8_dequantize(qo, so), oracle.mx_dequantize(qb, sb))
+    check_product(host(c), yref, S, True, f"dynamic w4a8 {m}x{n}x{k} vs oracle",
+                  w4a8_block_sum_allowance(qo, so, qb, sb))
+
+
+def test_w4a8_dynamic_edge_activations():
+    m, n, k = 16, 300, 1024
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, ::3] = 2.0 ** -133
+    x[3] = 2.0 ** -126 * rng.integers(-3, 4, size=k)
+    x[4] = np.float32(3.0e38) * np.sign(rng.standard_normal(k))
+    x[5] = 0.25 * rng.integers(-24, 25, size=k)
+    x[15] = 448.0 * 2.0 ** rng.integers(-20, 20, size=k)  # E4M3 saturation edges
+    xb = synth.f32_to_bf16_bits(x)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 2).astype(np.float32))
+    qb, sb = mxq.quantize(dev(w))
+    qa, sa = mxq.quantize_fp8(dev(xb))
+    for dt in (torch.float32, torch.bfloat16):
+        c = mxq.gemm_w4a8_dynamic(dev(xb), qb, sb, dt)
+        assert same_bits(c, mxq.gemm_w4a8(qa, sa, qb, sb, dt)), f"edge activations w4a8 {dt}"
+
+
 def test_w4a4_dynamic_full_size():
     """The 28672 x 8192 decode weight, 16 bf16 activation rows: the whole
     output equals quantize + gemm, sampled columns against the oracle."""
@@ -834,6 +877,9 @@ def test_w4a4_dynamic_full_size():
     c = mxq.gemm_w4a4_dynamic(xd, qd, sd, torch.bfloat16)
     qa, sa = mxq.quantize(xd)
     assert same_bits(c, mxq.gemm_w4a4(qa, sa, qd, sd, torch.bfloat16)), "full size: differs from quantize + gemm"
+    c8 = mxq.gemm_w4a8_dynamic(xd, qd, sd, torch.bfloat16)
+    qa8, sa8 = mxq.quantize_fp8(xd)
+    assert same_bits(c8, mxq.gemm_w4a8(qa8, sa8, qd, sd, torch.bfloat16)), "full size: w4a8 dynamic differs"
     n = qo.shape[0]
     rng = np.random.default_rng(500)
     cols = np.unique(np.concatenate([rng.choice(n, size=256, replace=False), [0, n - 1]]))
@@ -933,7 +979,7 @@ def test_w4a4_quant_full_size_and_empty_k():
                                         ("w4a4", 40, 70, (1 << 20) + 32), ("w4a8", 16, 130, 1 << 20),
                                         ("w4a8", 260, 300, 1 << 20), ("w4a8", 40, 70, (1 << 20) + 32),
                                         ("gemv", 1, 7, 1 << 20), ("gemv", 3, 300, 1 << 20),
-                                        ("dyn", 16, 130, 1 << 20)])
+                                        ("dyn", 16, 130, 1 << 20), ("dyn8", 16, 130, 1 << 20)])
 def test_products_long_k(kind, m, n, k):
     rng = np.random.default_rng(m + n + k)
     qb = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
@@ -959,7 +1005,7 @@ def test_products_long_k(kind, m, n, k):
         if kind == "gemv":
             c = host(mxq.gemv_w4a16(dev(qb), dev(sb), dev(x), torch.float32))
             ad = oracle.to_f64(x[rows])
-        else:
+        elif kind == "dyn":
             xd, qbd, sbd = dev(x), dev(qb), dev(sb)
             cd = mxq.gemm_w4a4_dynamic(xd, qbd, sbd, torch.float32)
             qa_d, sa_d = mxq.quantize(xd)
@@ -967,6 +1013,15 @@ def test_products_long_k(kind, m, n, k):
             c = host(cd)
             qx, sx = oracle.mx_quantize(x[rows])
             ad = oracle.mx_dequantize(qx, sx)
+        else:
+            xd, qbd, sbd = dev(x), dev(qb), dev(sb)
+            cd = mxq.gemm_w4a8_dynamic(xd, qbd, sbd, torch.float32)
+            qa_d, sa_d = mxq.quantize_fp8(xd)
+            assert same_bits(cd, mxq.gemm_w4a8(qa_d, sa_d, qbd, sbd, torch.float32)), "long k: dynamic w4a8"
+            c = host(cd)
+            qx, sx = oracle.mx8_quantize(x[rows])
+            ad = oracle.mx8_dequantize(qx, sx)
+            extra = w4a8_block_sum_allowance(qx, sx, qb[cols], sb[cols])
     yref, S = oracle.gemm_nt(ad, bd)
     worst = check_product(c[np.ix_(rows, cols)], yref, S, False, f"{kind} {m}x{n}x{k}", extra)
     say(f"{kind} {m}x{n}x{k}: worst |err|/S {worst:.3g}")
