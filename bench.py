@@ -10,8 +10,8 @@ already resident in HBM:
          TransFP4 block quantize (rotation, bf16 residual, NVFP4/INT4 choice)
          of the same tensor and its dequantization
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16;
-         on the same weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x) and
-         W4A4 from bf16 x quantized inside the GEMM (the small-m kernel)
+         on the same weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x), and
+         both from bf16 x quantized inside the GEMM (the small-m kernel)
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
          (bf16 output, and MXFP4 output quantized in the epilogue); MXFP8
          quantize of the same A + W4A8 GEMM 8192^3 (E4M3 x E2M1 MFMA)
@@ -195,6 +195,9 @@ def main():
                     mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2))
         ops.append(("decode_w4a4_dynamic_m16", rotating([(q, s) for q, s in copies],
                                                         lambda q, s: mxq.gemm_w4a4_dynamic(x16, q, s, c=y16)),
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2))
+        ops.append(("decode_w4a8_dynamic_m16", rotating([(q, s) for q, s in copies],
+                                                        lambda q, s: mxq.gemm_w4a8_dynamic(x16, q, s, c=y16)),
                     mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2))
     if "w4a4" in parts:
         a4, b4 = synth.w4a4_operands()
