@@ -1,6 +1,7 @@
-// mxq_gemm_common.h -- device helpers shared by the block-scaled MFMA
-// products (W4A4 and W4A8): direct global -> LDS copies, wait-count and
-// scheduling hints, and the LDS-staged epilogue stores.
+// mxq_gemm_common.h -- device helpers shared by the product kernels (W4A4,
+// W4A8, W4A16 and the small-m kernels): direct global / buffer -> LDS
+// copies, wait counts and scheduling hints, and the LDS-staged epilogue
+// stores.
 #pragma once
 #include "mxq_device.h"
 

@@ -762,7 +762,7 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 
 // ---------------------------------------------------------------------------
 // Decode kernel for m <= 16, k % 512 == 0 (MXFP4): the weight stream is
-// moved by direct global -> LDS loads, so the bytes in flight are bounded by
+// moved by direct buffer -> LDS copies, so the bytes in flight are bounded by
 // LDS, not by staging registers, and the arithmetic is the 16x16x32 bf16
 // MFMA (its cost does not grow with m; rows m..15 of the activation operand
 // read a shared zero row).
