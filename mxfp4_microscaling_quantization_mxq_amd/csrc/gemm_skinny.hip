@@ -26,9 +26,9 @@
 // operands (the E4M3 x E2M1 group sums are truncated; see the W4A8 entry
 // point).
 //
-//   * Block = NW waves; wave w owns WT 16-row weight tiles (rows n0 + 16 WT w
-//     ..) for all of k, which runs in stages of KS = 512 or 256 through an
-//     NR-deep LDS ring filled by buffer -> LDS copies.
+//   * Block = NW waves; wave w owns weight rows n0 + 16 w .. +16 for all of
+//     k, which runs in stages of KS = 512 or 256 through an NR-deep LDS ring
+//     filled by buffer -> LDS copies.
 //   * The activation rows' codes and scales of a stage (MT rows, shared by
 //     all waves) ride in the same ring slot.  Every wave issues the same
 //     number of copies; surplus ones land in scratch rows, so the wait
@@ -75,40 +75,37 @@ __device__ __forceinline__ int skinny_rotation(int64_t k) {
 // One ring slot.  Each slot is its own LDS variable and every slot index is
 // a compile-time constant, so the compiler can tell that reads of one slot
 // do not touch the slots whose copies are in flight.
-template <int MT, int NW, int WT, int KS, bool kFp8>
+template <int MT, int NW, int KS, bool kFp8>
 struct SkSlot {
   using G = SkGeom<KS, kFp8>;
-  uint8_t w[16 * WT * NW * G::RowB];     // weight codes
+  uint8_t w[16 * NW * G::RowB];          // weight codes
   uint8_t x[(MT + G::XRPI) * G::XRowB];  // activation codes, one copy's worth of scratch rows
   // Scales: a 256-byte region per 16 rows (one 64-lane dword copy), row r
   // of a group at (r % 16) * ScB; with 8 scale bytes per row the upper half
   // of a region is scratch.
-  uint8_t ws[WT * NW * 256];             // weight scales
+  uint8_t ws[NW * 256];                  // weight scales
   uint8_t xs[(MT / 16 + 1) * 256];       // activation scales, one scratch region
 };
-template <int MT, int NW, int WT, int KS, bool kFp8, int B>
-__device__ __forceinline__ SkSlot<MT, NW, WT, KS, kFp8>& sk_slot() {
-  __shared__ __attribute__((aligned(1024))) SkSlot<MT, NW, WT, KS, kFp8> slot;
+template <int MT, int NW, int KS, bool kFp8, int B>
+__device__ __forceinline__ SkSlot<MT, NW, KS, kFp8>& sk_slot() {
+  __shared__ __attribute__((aligned(1024))) SkSlot<MT, NW, KS, kFp8> slot;
   return slot;
 }
 
-// WT = 16-row weight tiles per wave: with two, every activation fragment
-// read from LDS feeds two MFMAs.
-template <bool kFp8, int MT, int NW, int WT, int NR, int KS, bool kBf16Out>
+template <bool kFp8, int MT, int NW, int NR, int KS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
                                                            const uint8_t* __restrict__ bq,
                                                            const uint8_t* __restrict__ bs, int64_t m,
                                                            int64_t n, int64_t k, void* __restrict__ c) {
   using G = SkGeom<KS, kFp8>;
-  using Slot = SkSlot<MT, NW, WT, KS, kFp8>;
-  constexpr int WR = 16 * WT;                        // weight rows per wave
-  constexpr int RB = WR * NW;                        // weight rows per block
+  using Slot = SkSlot<MT, NW, KS, kFp8>;
+  constexpr int RB = 16 * NW;                        // weight rows per block
   constexpr int MTT = MT / 16;                       // 16-row activation tiles
-  constexpr int WC = WR / G::RPI;                    // weight code copies per wave
+  constexpr int WC = 16 / G::RPI;                    // weight code copies per wave
   constexpr int XC = (MT / G::XRPI + NW - 1) / NW;   // activation code copies per wave
   constexpr int XS = (MT / 16 + NW - 1) / NW;        // activation scale copies per wave (16 rows each)
-  constexpr int D = WC + WT + XC + XS;               // copies per wave per stage
+  constexpr int D = WC + 1 + XC + XS;                // copies per wave per stage
   constexpr int WSW = swz(G::U), XSW = swz(G::XU);   // swizzle periods
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -122,11 +119,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   // Lane offsets of the copies, fixed for the whole k loop (a stage only
   // moves the uniform offset).  Rows past the operand are clamped to its
   // last row: the copy stays in bounds and fills an LDS row nobody stores.
-  unsigned offw[WC], offws[WT], offx[XC], offxs[XS];
+  unsigned offw[WC], offx[XC], offxs[XS];
   int dx[XC], dxs[XS];
 #pragma unroll
   for (int q = 0; q < WC; q++) {
-    const int row = WR * wave + G::RPI * q + lane / G::U;
+    const int row = 16 * wave + G::RPI * q + lane / G::U;
     const unsigned unit = (unsigned)((lane % G::U) ^ (row % WSW));
     offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
   }
@@ -135,9 +132,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   // the region's scratch half
   const int srow = (lane % (16 * G::LPR)) / G::LPR;
   const unsigned spart = 4u * (unsigned)(lane % G::LPR);
-#pragma unroll
-  for (int r = 0; r < WT; r++)
-    offws[r] = (unsigned)min(WR * wave + 16 * r + srow, rows_w - 1) * (unsigned)ks + spart;
+  const unsigned offws = (unsigned)min(16 * wave + srow, rows_w - 1) * (unsigned)ks + spart;
 #pragma unroll
   for (int j = 0; j < XC; j++) {
     const int a = wave + NW * j;  // copy slot (wave-uniform): activation rows XRPI a ..
@@ -163,26 +158,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   // the same copies.
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    Slot& sl = sk_slot<MT, NW, WT, KS, kFp8, B>();
+    Slot& sl = sk_slot<MT, NW, KS, kFp8, B>();
     const int sl0 = min(s, nst - 1);
     const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
     for (int q = 0; q < WC; q++)
-      bdma16(rw, offw[q], sc * G::RowB, sl.w + (WR * wave + G::RPI * q) * G::RowB);
-#pragma unroll
-    for (int r = 0; r < WT; r++) bdma4(rws, offws[r], sc * G::ScB, sl.ws + 256 * (WT * wave + r));
+      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+    bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
 #pragma unroll
     for (int j = 0; j < XS; j++) bdma4(rxs, offxs[j], sc * G::ScB, sl.xs + dxs[j]);
   };
 
-  f32x4 acc[WT][MTT];
+  f32x4 acc[MTT];
 #pragma unroll
-  for (int r = 0; r < WT; r++)
-#pragma unroll
-    for (int t = 0; t < MTT; t++) acc[r][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int wrow = WR * wave + col;  // this lane's block weight row in tile 0 (+16 r in tile r)
+  for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int wrow = 16 * wave + col;  // this lane's block weight row
   // scale bytes of a row as words: word i holds blocks 4i .. 4i+3
   auto scale_words = [&](const uint8_t* p, unsigned (&wds)[G::STEPS]) {
     if constexpr (G::STEPS == 4) {
@@ -206,31 +198,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   };
   auto compute = [&](auto slot_tag) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = sk_slot<MT, NW, WT, KS, kFp8, B>();
-    unsigned wss[WT][G::STEPS], xss[MTT][G::STEPS];
-#pragma unroll
-    for (int r = 0; r < WT; r++) scale_words(sl.ws + 256 * (WT * wave + r) + col * G::ScB, wss[r]);
+    const Slot& sl = sk_slot<MT, NW, KS, kFp8, B>();
+    unsigned wss[G::STEPS], xss[MTT][G::STEPS];
+    scale_words(sl.ws + 256 * wave + col * G::ScB, wss);
 #pragma unroll
     for (int t = 0; t < MTT; t++) scale_words(sl.xs + 256 * t + col * G::ScB, xss[t]);
 #pragma unroll
     for (int i = 0; i < G::STEPS; i++) {
       const int wslot = ((4 * i + g) ^ (col % WSW)) << 4;  // weight unit 4i+g of a row r, r % 16 == col
-      i32x8 wf[WT];
-      int sw[WT];
-#pragma unroll
-      for (int r = 0; r < WT; r++) {
-        const u32x4 cw = *(const u32x4*)(sl.w + (wrow + 16 * r) * G::RowB + wslot);
-        wf[r] = (i32x8){(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
-        sw[r] = (int)((wss[r][i] >> (8 * g)) & 0xFFu);
-      }
+      const u32x4 cw = *(const u32x4*)(sl.w + wrow * G::RowB + wslot);
+      const i32x8 wf = {(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
+      const int sw = (int)((wss[i] >> (8 * g)) & 0xFFu);
 #pragma unroll
       for (int t = 0; t < MTT; t++) {
         const i32x8 xf = x_fragment(sl.x + (16 * t + col) * G::XRowB, i);
         const int sx = (int)((xss[t][i] >> (8 * g)) & 0xFFu);
-#pragma unroll
-        for (int r = 0; r < WT; r++)
-          acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf[r], acc[r][t], kFp8 ? kFmtFp8 : kFmtFp4,
-                                                                      kFmtFp4, 0, sx, 0, sw[r]);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf, wf, acc[t], kFp8 ? kFmtFp8 : kFmtFp4, kFmtFp4,
+                                                                  0, sx, 0, sw);
       }
     }
   };
@@ -263,11 +247,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   }
   wait_vmcnt<0>();
 
-  // lane holds c[16t + 4g + e][n0 + wrow + 16r]
-#pragma unroll
-  for (int r = 0; r < WT; r++) {
-    const int64_t nn = n0 + wrow + 16 * r;
-    if (nn >= n) continue;
+  // lane holds c[16t + 4g + e][n0 + wrow]
+  const int64_t nn = n0 + wrow;
+  if (nn < n) {
 #pragma unroll
     for (int t = 0; t < MTT; t++)
 #pragma unroll
@@ -275,24 +257,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
         const int64_t mm = 16 * t + 4 * g + e;
         if (mm >= m) continue;
         if (kBf16Out)
-          ((uint16_t*)c)[mm * n + nn] = f32_to_bf16_rne(acc[r][t][e]);
+          ((uint16_t*)c)[mm * n + nn] = f32_to_bf16_rne(acc[t][e]);
         else
-          ((float*)c)[mm * n + nn] = acc[r][t][e];
+          ((float*)c)[mm * n + nn] = acc[t][e];
       }
   }
 }
 
-template <bool kFp8, int MT, int NW, int WT, int NR, int KS>
+template <bool kFp8, int MT, int NW, int NR, int KS>
 static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  constexpr int RB = 16 * WT * NW;
-  const dim3 grid((unsigned)((n + RB - 1) / RB));
+  const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, WT, NR, KS, true>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs,
-                       m, n, k, c);
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs, m,
+                       n, k, c);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, WT, NR, KS, false>), grid, dim3(64 * NW), 0, st, aq, as, bq,
-                       bs, m, n, k, c);
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs, m,
+                       n, k, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,32 +502,32 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   }
 }
 
-// Launch configurations <MT, NW, WT, NR, KS> per activation tile.  The LDS
+// Launch configurations <MT, NW, NR, KS> per activation tile.  The LDS
 // ring holds at most 160 KiB: the 128-row tile of E2M1 activations fits
 // two 512-k stages, the 64- and 128-row E4M3 tiles take 256-k stages.
 #ifndef MXQ_SK4_C16
-#define MXQ_SK4_C16 16, 7, 1, 3, 512
+#define MXQ_SK4_C16 16, 7, 3, 512
 #endif
 #ifndef MXQ_SK4_C32
-#define MXQ_SK4_C32 32, 7, 1, 3, 512
+#define MXQ_SK4_C32 32, 7, 3, 512
 #endif
 #ifndef MXQ_SK4_C64
-#define MXQ_SK4_C64 64, 7, 1, 3, 512
+#define MXQ_SK4_C64 64, 7, 3, 512
 #endif
 #ifndef MXQ_SK4_C128
-#define MXQ_SK4_C128 128, 7, 1, 2, 512
+#define MXQ_SK4_C128 128, 7, 2, 512
 #endif
 #ifndef MXQ_SK8_C16
-#define MXQ_SK8_C16 16, 7, 1, 3, 512
+#define MXQ_SK8_C16 16, 7, 3, 512
 #endif
 #ifndef MXQ_SK8_C32
-#define MXQ_SK8_C32 32, 7, 1, 3, 512
+#define MXQ_SK8_C32 32, 7, 3, 512
 #endif
 #ifndef MXQ_SK8_C64
-#define MXQ_SK8_C64 64, 7, 1, 4, 256
+#define MXQ_SK8_C64 64, 7, 4, 256
 #endif
 #ifndef MXQ_SK8_C128
-#define MXQ_SK8_C128 128, 7, 1, 3, 256
+#define MXQ_SK8_C128 128, 7, 3, 256
 #endif
 
 bool gemm_skinny_applies(int64_t m, int64_t k) {
