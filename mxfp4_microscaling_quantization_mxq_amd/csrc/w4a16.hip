@@ -59,14 +59,16 @@ __device__ __forceinline__ void dequant_chunk(u32x4 c, unsigned sbytes, bf16x8 w
 
 // Loads of one lane for one (row tile, chunk): 16 code bytes and the scale
 // byte(s).  Invalid lanes read a valid dummy address and are zeroed by a
-// select, so the load sequence has no branches.
-template <bool kNv, bool kLoadScale = true>
+// select, so the load sequence has no branches.  kWide: NVFP4 rows known to
+// be 16-byte aligned (k % 32 == 0) and the chunk whole, one 16-byte load.
+template <bool kNv, bool kLoadScale = true, bool kWide = false>
 __device__ __forceinline__ void load_chunk(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
                                            int64_t row, int64_t kb, bool valid, bool khi, int64_t kq, int64_t ks,
                                            u32x4& codes, unsigned& sc) {
+  static_assert(!(kNv && kWide && kLoadScale), "the wide NVFP4 load takes its scales from the staged copy");
   const int64_t r = valid ? row : 0;
   const int64_t b = valid ? kb : 0;
-  if (!kNv) {
+  if (!kNv || kWide) {
     u32x4 c = __builtin_nontemporal_load((const u32x4*)(wq + r * kq + b / 2));
     codes = valid ? c : (u32x4){0u, 0u, 0u, 0u};
     if (kLoadScale) {
@@ -192,10 +194,12 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
   static_assert(RB % U == 0, "rows per block must be a multiple of the unroll");
   // per-wave partial sums: red[wave][act row][weight row][lane]
   __shared__ float red[W][M][RB][64];
-  // MXFP4 scale bytes of a wave's 8 rows x 64 blocks, fetched with one
-  // 8-byte-per-lane load instead of eight 1-byte-per-lane loads (those
-  // small requests cost about 10 % of the decode time)
-  __shared__ uint8_t sstage[W][8][64];
+  // Scale bytes of a wave's 8 rows for its 2048-k range (64 MXFP4 or 128
+  // NVFP4 blocks per row), fetched with one 8- or 16-byte-per-lane load
+  // instead of eight 1- or 2-byte-per-lane loads (those small requests cost
+  // about 10 % of the MXFP4 decode time)
+  constexpr int SB = kNv ? 128 : 64;  // scale bytes per row per range
+  __shared__ __attribute__((aligned(16))) uint8_t sstage[W][8][SB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int64_t kq = k / 2;                   // code bytes per row
@@ -227,22 +231,41 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
     for (int r0 = 0; r0 < RB; r0 += U) {
       u32x4 codes[U];
       unsigned sc[U];
-      // fast scale path: MXFP4, 8 rows per step, this wave's 2048-k range
-      // whole and every row's scale segment 8-byte aligned
-      const bool stage_sc = !kNv && U == 8 && (kr + 1) * 64 <= ks && ks % 8 == 0;
+      // fast scale path: 8 rows per step, this wave's 2048-k range whole
+      // and every row's scale segment aligned to the per-lane load (8 B
+      // MXFP4, 16 B NVFP4; NVFP4 rows are then 16-byte aligned too)
+      const bool stage_sc = U == 8 && (kr + 1) * SB <= ks && ks % (SB / 8) == 0;
       if (stage_sc) {
         const int rr = lane >> 3;
         const int64_t srow = n0 + r0 + rr;
-        const u32x2 sv = *(const u32x2*)(ws + (srow < n ? srow : 0) * ks + kr * 64 + 8 * (lane & 7));
+        const uint8_t* sp = ws + (srow < n ? srow : 0) * ks + kr * SB + (SB / 8) * (lane & 7);
+        u32x4 sv;
+        if (kNv) {
+          sv = *(const u32x4*)sp;
+        } else {
+          const u32x2 s2 = *(const u32x2*)sp;
+          sv = (u32x4){s2.x, s2.y, 0u, 0u};
+        }
 #pragma unroll
         for (int u = 0; u < U; u++) {
           const int64_t row = n0 + r0 + u;
-          load_chunk<kNv, false>(wq, ws, row, kb, kval && row < n, khi, kq, ks, codes[u], sc[u]);
+          load_chunk<kNv, false, kNv>(wq, ws, row, kb, kval && row < n, khi, kq, ks, codes[u], sc[u]);
         }
-        *(u32x2*)&sstage[wave][rr][8 * (lane & 7)] = sv;
-        // the wave reads back what it wrote: one wave's LDS operations run in order
+        if (kNv)
+          *(u32x4*)&sstage[wave][rr][16 * (lane & 7)] = sv;
+        else
+          *(u32x2*)&sstage[wave][rr][8 * (lane & 7)] = (u32x2){sv.x, sv.y};
+        // the wave reads back what it wrote: one wave's LDS operations run in
+        // order.  NVFP4: the lane's two blocks (halves of its 32 k) as one
+        // 16-bit pair, low byte first.
 #pragma unroll
-        for (int u = 0; u < U; u++) sc[u] = (n0 + r0 + u < n) ? (unsigned)sstage[wave][u][lane] : 127u;
+        for (int u = 0; u < U; u++) {
+          const bool v = n0 + r0 + u < n;
+          if (kNv)
+            sc[u] = v ? (unsigned)*(const uint16_t*)&sstage[wave][u][2 * lane] : 0u;
+          else
+            sc[u] = v ? (unsigned)sstage[wave][u][lane] : 127u;
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < U; u++) {
@@ -771,8 +794,9 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     bytes per row, 1 KiB of activations per activation row) through a ring
 //     of NR LDS stages.
 //   * Every wave loads its own rows' codes (4 x 1 KiB, four 256-B row
-//     segments per instruction) and scales (one 4-byte-per-lane instruction
-//     = 16 rows x 16 B), and its share of the activation rows (one 1 KiB
+//     segments per instruction) and scales (16 rows x 16 B of E8M0, one
+//     4-byte-per-lane instruction; NVFP4: 16 rows x 32 B of E4M3, two), and
+//     its share of the activation rows (one 1 KiB
 //     instruction per row; every wave issues the same number, surplus ones
 //     fill a scratch row, so the wait counts are compile-time constants).
 //   * LDS swizzles (applied on the global side of the copy): code unit u of
@@ -780,8 +804,9 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     u ^ (i & 15).  The 16 lanes of a fragment read touch 16 distinct bank
 //     groups.
 //   * Fragments: lane (col = l % 16, g = l / 16) takes code unit 4i + g of
-//     its weight row (32 k = one MXFP4 block, i = 0..3), expands it with the
-//     scaled convert to four exact bf16x8 operands, and pairs operand j with
+//     its weight row (32 k = one MXFP4 block or two NVFP4 blocks, i =
+//     0..3), expands it to four exact bf16x8 operands (dequant_chunk), and
+//     pairs operand j with
 //     activation unit 16i + 4g + j of activation row col (the MFMA k slots
 //     are a permutation of the stage's k, the same on both sides).
 //   * One s_barrier per stage (after the wave's own copies of stage s have
@@ -793,10 +818,12 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     column offsets instead of all at the same one (about 10 % faster on
 //     a 28672 x 8192 weight).  The k order of a block's sum changes with
 //     its rotation; the result is still one fixed order per output row.
+//   * NVFP4: the tensor scale multiplies the fp32 sums in the epilogue.
 constexpr int kDdK = 512;             // k per stage
 constexpr int kDdRowB = kDdK / 2;     // code bytes per row per stage
-constexpr int kDdScB = kDdK / 32;     // scale bytes per row per stage
 constexpr int kDdXRowB = kDdK * 2;    // activation bytes per row per stage
+template <bool kNv>
+constexpr int dd_scale_bytes() { return kNv ? kDdK / 16 : kDdK / 32; }  // per row per stage
 
 
 // One ring slot: codes, activations and scales of one stage.  Every slot is
@@ -804,42 +831,46 @@ constexpr int kDdXRowB = kDdK * 2;    // activation bytes per row per stage
 // constant, so the compiler can tell that the reads of slot b do not touch
 // the slots whose copies are still in flight (one shared array would make it
 // wait for every outstanding copy before the first read).
-template <int MT, int NW>
+template <int MT, int NW, bool kNv>
 struct DdSlot {
   uint8_t w[16 * NW * kDdRowB];
   uint8_t x[(MT + 2) * kDdXRowB];  // MT activation rows, a zero row, a scratch row
-  uint8_t s[16 * NW * kDdScB];
+  uint8_t s[16 * NW * dd_scale_bytes<kNv>()];
 };
-template <int MT, int NW, int B>
-__device__ __forceinline__ DdSlot<MT, NW>& dd_slot() {
-  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW> slot;
+template <int MT, int NW, bool kNv, int B>
+__device__ __forceinline__ DdSlot<MT, NW, kNv>& dd_slot() {
+  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW, kNv> slot;
   return slot;
 }
 
-template <int MT, int NW, int NR, bool kBf16Out>
+template <bool kNv, int MT, int NW, int NR, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* __restrict__ wq,
-                                                                const uint8_t* __restrict__ ws, int64_t n,
+                                                                const uint8_t* __restrict__ ws,
+                                                                const float* __restrict__ gscale, int64_t n,
                                                                 int64_t k, const uint16_t* __restrict__ x,
                                                                 int64_t m, void* __restrict__ y) {
+  using Slot = DdSlot<MT, NW, kNv>;
+  constexpr int ScB = dd_scale_bytes<kNv>();  // scale bytes per row per stage (16 or 32)
+  constexpr int SCP = ScB / 16;               // scale copies per wave (16 rows x 16 B each)
   constexpr int RB = 16 * NW;                 // weight rows per block
   constexpr int XPW = (MT + NW - 1) / NW;     // activation-row copies per wave per stage
-  constexpr int D = 4 + 1 + XPW;              // copies per wave per stage
+  constexpr int D = 4 + SCP + XPW;            // copies per wave per stage
   static_assert(NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
-  const int64_t kq = k / 2, ks = k / 32, kx = k * 2;
+  const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
   const int nst = (int)(k / kDdK);
   const int rot = (int)((blockIdx.x / 8) % (unsigned)nst);
 
   // zero rows (activation rows m..15 of the MFMA operand read them)
   for (int i = tid; i < kDdXRowB / 16; i += 64 * NW) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(dd_slot<MT, NW, 0>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, 1 % NR>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, 2 % NR>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, 3 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    *(u32x4*)(dd_slot<MT, NW, kNv, 0>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, kNv, 1 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, kNv, 2 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, kNv, 3 % NR>().x + MT * kDdXRowB + 16 * i) = z;
   }
   __syncthreads();
 
@@ -857,6 +888,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     const unsigned unit = (unsigned)((lane & 15) ^ (row & 15));
     offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
   }
+  // scale copy h covers 64 lanes x 4 B = 16 B of each of the wave's 16
+  // rows: lane i takes row i / 4, bytes 16 h + 4 (i % 4) .. +4
   const unsigned offs = (unsigned)min(16 * wave + (lane >> 2), rows_w - 1) * (unsigned)ks + 4u * (lane & 3);
 #pragma unroll
   for (int j = 0; j < XPW; j++) {
@@ -872,12 +905,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   const __amdgpu_buffer_rsrc_t rx = panel_rsrc(x, m * kx);
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
+    Slot& sl = dd_slot<MT, NW, kNv, B>();
     const int sl0 = min(s, nst - 1);
     const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
     for (int q = 0; q < 4; q++) bdma16(rw, offw[q], sc * kDdRowB, sl.w + (16 * wave + 4 * q) * kDdRowB);
-    bdma4(rs, offs, sc * kDdScB, sl.s + 16 * wave * kDdScB);
+    // LDS: scale piece h of the wave's rows at s + (SCP wave + h) * 256,
+    // row r of the wave at + 16 r (so row r's bytes 16 h.. sit in piece h)
+#pragma unroll
+    for (int h = 0; h < SCP; h++) bdma4(rs, offs + 16u * h, sc * ScB, sl.s + (SCP * wave + h) * 256);
 #pragma unroll
     for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * kDdXRowB, sl.x + xdst[j]);
   };
@@ -887,25 +923,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   const bool xreal = col < m;
   auto compute = [&](auto slot_tag) {
     constexpr int B = decltype(slot_tag)::value;
-    const DdSlot<MT, NW>& sl = dd_slot<MT, NW, B>();
+    const Slot& sl = dd_slot<MT, NW, kNv, B>();
     const uint8_t* xb = sl.x + (xreal ? col : MT) * kDdXRowB;
     const int xsw = xreal ? col : 0;
-    const u32x4 sv = *(const u32x4*)(sl.s + wrow * kDdScB);
-    const unsigned svs[4] = {sv.x, sv.y, sv.z, sv.w};
+    // this lane's row's scale bytes: 16 (E8M0 per 32 k) or 32 (E4M3 per 16)
+    unsigned svs[ScB / 4];
+#pragma unroll
+    for (int h = 0; h < SCP; h++) {
+      const u32x4 sv = *(const u32x4*)(sl.s + (SCP * wave + h) * 256 + 16 * col);
+      svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u32x4 cw = *(const u32x4*)(sl.w + wrow * kDdRowB + (((4 * i + g) ^ col) << 4));
-      const float scale = e8m0_as_scale((svs[i] >> (8 * g)) & 0xFFu);
-      const unsigned d[4] = {cw.x, cw.y, cw.z, cw.w};
+      bf16x8 wf[4];
+      if constexpr (kNv) {
+        // the two E4M3 scales of chunk 4i + g: bytes 8i + 2g, 8i + 2g + 1
+        dequant_chunk<true>(cw, (svs[2 * i + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu, wf);
+      } else {
+        dequant_chunk<false>(cw, (svs[i] >> (8 * g)) & 0xFFu, wf);
+      }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const bf16x8 xa = *(const bf16x8*)(xb + ((16 * i + ((4 * g + j) ^ xsw)) << 4));
-        bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
-        bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
-        bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
-        bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
-        const bf16x8 wf = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wf, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wf[j], acc, 0, 0, 0);
       }
     }
   };
@@ -945,39 +986,47 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   wait_vmcnt<0>();
 
   // lane holds y[4g + i][n0 + wrow]
+  const float st = kNv ? *gscale : 1.0f;
   const int64_t nn = n0 + wrow;
   if (nn < n) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int64_t mm = 4 * g + i;
       if (mm >= m) continue;
+      const float o = kNv ? acc[i] * st : acc[i];
       if (kBf16Out)
-        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(acc[i]);
+        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(o);
       else
-        ((float*)y)[mm * n + nn] = acc[i];
+        ((float*)y)[mm * n + nn] = o;
     }
   }
 }
 
-template <int MT, int NW, int NR>
-static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, int64_t n, int64_t k, const void* x, int64_t m,
-                              void* y, bool bf16_out, hipStream_t st) {
+template <bool kNv, int MT, int NW, int NR>
+static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
+                              const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_decode_dma<MT, NW, NR, true>), grid, dim3(64 * NW), 0, st, wq, ws, n, k,
-                       (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, true>), grid, dim3(64 * NW), 0, st, wq, ws, gscale, n,
+                       k, (const uint16_t*)x, m, y);
   else
-    hipLaunchKernelGGL((k_w4a16_decode_dma<MT, NW, NR, false>), grid, dim3(64 * NW), 0, st, wq, ws, n, k,
-                       (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, false>), grid, dim3(64 * NW), 0, st, wq, ws, gscale,
+                       n, k, (const uint16_t*)x, m, y);
 }
 
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  if (!nv && m >= 2 && m <= 16 && k % kDdK == 0 && k <= (1 << 24) && n >= 16 * 7 * 128) {
+  // The decode ring from m = 2 (MXFP4) or m = 4 (NVFP4): the NVFP4 dequant
+  // costs vector-ALU work per weight element in the ring, while the
+  // vector-ALU kernel applies each E4M3 scale once per 16 products (measured
+  // on 28672 x 8192: m = 2 29.5 vs 40-45 us, m = 4 47-50 vs 39-41 us).
+  if (m >= (nv ? 4 : 2) && m <= 16 && k % kDdK == 0 && k <= (1 << 24) && n >= 16 * 7 * 128) {
     if (m <= 4)
-      launch_decode_dma<4, 7, 3>(wq, ws, n, k, x, m, y, bf16_out, st);
+      nv ? launch_decode_dma<true, 4, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
+         : launch_decode_dma<false, 4, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
     else
-      launch_decode_dma<16, 7, 3>(wq, ws, n, k, x, m, y, bf16_out, st);
+      nv ? launch_decode_dma<true, 16, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
+         : launch_decode_dma<false, 16, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (!nv && m >= 5 && m <= 16) {
     const dim3 grid((unsigned)((n + 63) / 64));
     if (bf16_out)

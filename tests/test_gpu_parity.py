@@ -668,6 +668,48 @@ def test_nv_gemm_ragged():
             check_product(y, yref, S, dt == torch.bfloat16, f"nv gemm n={n} k={k} m={m}")
 
 
+# NVFP4 weights at decode sizes: the staged-scale path of the m <= 4 kernel
+# (k % 256 == 0, whole 2048-k ranges; a partial last range and k % 32 == 16
+# take the byte-wise path), and the m = 2..16 ring kernel (n >= 14336,
+# k % 512 == 0) with ragged weight rows.
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
+                                   (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16)])
+def test_nv_decode_paths(n, k, m):
+    w = laplace_bf16(n + 3 * k + m, n, k)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(k + m).standard_normal((m, k)).astype(np.float32))
+    qo, so, go = assert_nv(w, None, f"nv decode W {n}x{k}")
+    g = torch.tensor([go], dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(n + m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=min(n, 300), replace=False), [0, n - 1]]))
+    yref, S = oracle.gemm_nt(oracle.to_f64(x), oracle.nv_dequantize(qo[cols], so[cols], go))
+    for dt in (torch.float32, torch.bfloat16):
+        y = host(mxq.nv_gemm(dev(qo), dev(so), g, dev(x), dt))
+        check_product(y[:, cols], yref, S, dt == torch.bfloat16, f"nv decode n={n} k={k} m={m} {dt}")
+
+
+@functools.lru_cache(maxsize=1)
+def decode_weight_nv():
+    w, _ = synth.decode_gemv(1)
+    return oracle.nv_quantize(w)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_nv_decode_full_size_sampled(m):
+    """The 28672 x 8192 decode weight in NVFP4 at m = 1, 4, 16."""
+    qo, so, go = decode_weight_nv()
+    _, x = synth.decode_gemv(m)
+    n = qo.shape[0]
+    g = torch.tensor([go], dtype=torch.float32, device="cuda")
+    args = (dev(qo), dev(so), g, dev(x))
+    y = host(mxq.nv_gemm(*args, torch.bfloat16))
+    assert np.array_equal(y, host(mxq.nv_gemm(*args, torch.bfloat16))), "run-to-run determinism"
+    rng = np.random.default_rng(600 + m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=384, replace=False), [0, n - 1]]))
+    yref, S = oracle.gemm_nt(oracle.to_f64(x), oracle.nv_dequantize(qo[cols], so[cols], go))
+    worst = check_product(y[:, cols], yref, S, True, f"nv decode m={m}")
+    say(f"nv decode m={m}: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
+
+
 def test_nv_vs_mx_full_size_sampled():
     """NVFP4 and MXFP4 W4A16 GEMM on the 8192x4096 weight and 4096x4096
     activations, outputs sampled; NMSE / cosine of each format reported."""
