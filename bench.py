@@ -9,7 +9,8 @@ already resident in HBM:
          with the 32-point block Hadamard rotation fused ahead of it; the
          TransFP4 block quantize (rotation, bf16 residual, NVFP4/INT4 choice)
          of the same tensor and its dequantization
-  gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16;
+  gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
+         (and the same weight in NVFP4 at m = 1, 16);
          on the same weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x), and
          both from bf16 x quantized inside the GEMM (the small-m kernel)
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
@@ -170,7 +171,7 @@ def main():
         w2, _ = synth.decode_gemv(1)
         w2d = to_dev(w2)
         q2, s2 = mxq.quantize(w2d)
-        del w2d, w2
+        del w2d
         nc = ncopies(mx_bytes(n2, k2))
         copies = [(q2, s2)] + [(q2.clone(), s2.clone()) for _ in range(nc - 1)]
         for m in (1, 4, 16):
@@ -179,6 +180,18 @@ def main():
             ops.append((f"gemv_w4a16_m{m}",
                         rotating([(q, s, xm, ym) for q, s in copies], lambda q, s, x, y: mxq.gemv_w4a16(q, s, x, y=y)),
                         gemv_bytes(n2, k2, m), 2 * m * n2 * k2))
+        # the same weight in NVFP4 (E4M3 per 16 + fp32 tensor scale)
+        qn2, sn2, gn2 = mxq.nv_quantize(to_dev(w2))
+        del w2
+        ncn = ncopies(nv_bytes(n2, k2))
+        ncopies_nv = [(qn2, sn2)] + [(qn2.clone(), sn2.clone()) for _ in range(ncn - 1)]
+        for m in (1, 16):
+            xm = to_dev(synth.decode_gemv(m)[1])
+            ym = torch.empty((m, n2), dtype=bf16, device=dev)
+            ops.append((f"nv_gemv_w4a16_m{m}",
+                        rotating([(q, s) for q, s in ncopies_nv],
+                                 lambda q, s, x=xm, y=ym: mxq.nv_gemm(q, s, gn2, x, y=y)),
+                        nv_bytes(n2, k2) + m * k2 * 2 + m * n2 * 2, 2 * m * n2 * k2))
         # decode-sized W4A4 / W4A8 on the same weight (the small-m kernel:
         # the weight stream bounds it), and W4A4 straight from bf16
         # activations with their quantization fused into the GEMM
