@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__
     }
 }
 
-constexpr int kBM = 256, kBN = 256;  // block tile of the ring kernel
+constexpr int kBM = 256;  // block tile rows of the ring kernel (columns: 256 or 128)
 
 // ---------------------------------------------------------------------------
 // Ring kernel (k % 1024 == 0).  Block tile 256 x 256; each wave multiplies
@@ -142,45 +142,48 @@ constexpr int kBM = 256, kBN = 256;  // block tile of the ring kernel
 //     row (a 4-byte fetch per row and stage made as many L2 requests as all
 //     the code bytes), double-buffered by pair.
 constexpr int kSB = 128;                   // code bytes per row per stage
-constexpr int kRStage = 2 * kBM * kSB;     // A, B codes of one stage
-constexpr int kRScale = 2 * kBM * 16;      // A, B scales of a stage pair (16 B per row)
 // Ring slots: each stage buffer and each scale-pair buffer is its own LDS
 // variable, addressed only through compile-time slot indices, so the
 // compiler can see that the fragment reads of one slot do not touch the
 // slot whose copy is in flight (with one shared array it would wait for
 // every outstanding copy before the first read, serializing copy and math).
-template <int B>
+// A slot holds the A then the B codes of one stage ((256 + BN) rows x 128
+// B); a scale slot the A then the B scales of a stage pair (16 B per row).
+template <int BN, int B>
 __device__ __forceinline__ uint8_t* w4_codes() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[kRStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[(kBM + BN) * kSB];
   return buf;
 }
-template <int B>
+template <int BN, int B>
 __device__ __forceinline__ uint8_t* w4_scales() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[kRScale];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[(kBM + BN) * 16];
   return buf;
 }
 
 // NWV waves per block: 4 (a 2 x 2 grid of 128 x 128 wave tiles, one wave
 // per SIMD) or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's
-// MFMAs cover the other's waits).
-template <int NWV, int OUT>
+// MFMAs cover the other's waits).  BN = 128 halves the tile's columns (8
+// waves of 128 x 32): twice the tiles where 256 x 256 leaves CUs idle.
+template <int NWV, int OUT, int BN>
 __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
                                                            const uint8_t* __restrict__ bq,
                                                            const uint8_t* __restrict__ bs, int64_t m, int64_t n,
                                                            int64_t k, void* __restrict__ c,
                                                            uint8_t* __restrict__ cs) {
-  static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
+  static_assert((NWV == 4 && BN == 256) || (NWV == 8 && (BN == 256 || BN == 128)), "tile / waves");
   constexpr int WNC = NWV / 2;        // wave columns
-  constexpr int WCOLS = kBN / WNC;    // output columns per wave
+  constexpr int WCOLS = BN / WNC;     // output columns per wave
   constexpr int JB = WCOLS / 32;      // B fragments per wave
-  constexpr int RPW = kBM / NWV;      // rows each wave copies per operand
-  constexpr int CJ = RPW / 8;         // copy instructions per operand per wave
+  constexpr int RPW = kBM / NWV;      // A rows each wave copies
+  constexpr int CJ = RPW / 8;         // A copy instructions per wave
+  constexpr int RPWB = BN / NWV;      // B rows each wave copies
+  constexpr int CJB = RPWB / 8;       // B copy instructions per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNC, wn = wave % WNC;
   const int half = lane >> 5, r32 = lane & 31;
 
-  const int64_t tm_n = (m + kBM - 1) / kBM, tn_n = (n + kBN - 1) / kBN;
+  const int64_t tm_n = (m + kBM - 1) / kBM, tn_n = (n + BN - 1) / BN;
   const int64_t tiles = tm_n * tn_n;
   int64_t tid_lin = blockIdx.x;
   if (tiles % 8 == 0) tid_lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   const int64_t gsz = (tm_n - g0) < group ? (tm_n - g0) : group;
   const int64_t tm = g0 + (tid_lin % per_group) % gsz;
   const int64_t tn = (tid_lin % per_group) / gsz;
-  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+  const int64_t m0 = tm * kBM, n0 = tn * BN;
 
   const int64_t kq = k / 2, ks = k / 32;
   const int nstages = (int)(k / 256);  // a multiple of 4 (k % 1024 == 0)
@@ -198,10 +201,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
 
   // rows of this tile that exist (the last tile may be partial: its missing
   // rows re-read the last row and are never stored)
-  const int rows_a = (int)min((int64_t)kBM, m - m0), rows_b = (int)min((int64_t)kBN, n - n0);
+  const int rows_a = (int)min((int64_t)kBM, m - m0), rows_b = (int)min((int64_t)BN, n - n0);
   // scale copies: 16 B per row per stage pair; with 4 waves each wave copies
   // 64 rows of A and of B, with 8 waves waves 0-3 copy A and 4-7 copy B
-  const int srow = NWV == 4 ? 64 * wave + lane : 64 * (wave & 3) + lane;
+  // (with BN = 128, waves 6-7 repeat waves 4-5: the same bytes to the same
+  // place, so every wave issues one copy)
+  const int srow = NWV == 4 ? 64 * wave + lane : 64 * ((wave & 3) % (wave < 4 ? 4 : BN / 64)) + lane;
   // codes through buffer resources over the tile's row panels (the launcher
   // keeps every panel below 2^31 bytes); per-lane offsets fixed for the k loop
   const __amdgpu_buffer_rsrc_t rA = panel_rsrc(aq + m0 * kq, rows_a * kq);
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   const uint8_t* gsa = as + min(m0 + srow, m - 1) * ks;
   const uint8_t* gsb = bs + min(n0 + srow, n - 1) * ks;
   // lane offsets of the CJ code copies per operand (fixed for the k loop)
-  unsigned offa[CJ], offb[CJ];
+  unsigned offa[CJ], offb[CJB];
 #pragma unroll
   for (int j = 0; j < CJ; j++) {
     // lane -> LDS row RPW w + 8j + lane/8, physical unit lane%8, logical unit
@@ -217,24 +222,30 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
     const int row = RPW * wave + 8 * j + (lane >> 3);
     const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
     offa[j] = (unsigned)min(row, rows_a - 1) * (unsigned)kq + cu16;
+  }
+#pragma unroll
+  for (int j = 0; j < CJB; j++) {
+    // B rows RPWB w + 8j + lane/8; RPWB w is a multiple of 16, so the swizzle
+    // unit is the same expression as for A
+    const int row = RPWB * wave + 8 * j + (lane >> 3);
+    const unsigned cu16 = (unsigned)(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
     offb[j] = (unsigned)min(row, rows_b - 1) * (unsigned)kq + cu16;
   }
 
   // codes of stage s into code slot CB: 2 CJ copies per wave (a stage past
   // the end is clamped to the last one: a re-read into a slot nobody reads)
   auto issue_codes = [&](auto cb_tag, int s) {
-    uint8_t* base = w4_codes<decltype(cb_tag)::value>();
+    uint8_t* base = w4_codes<BN, decltype(cb_tag)::value>();
     const unsigned soff = (unsigned)min(s, nstages - 1) * kSB;
 #pragma unroll
-    for (int j = 0; j < CJ; j++) {
-      bdma16(rA, offa[j], soff, base + (RPW * wave + 8 * j) * kSB);
-      bdma16(rB, offb[j], soff, base + kBM * kSB + (RPW * wave + 8 * j) * kSB);
-    }
+    for (int j = 0; j < CJ; j++) bdma16(rA, offa[j], soff, base + (RPW * wave + 8 * j) * kSB);
+#pragma unroll
+    for (int j = 0; j < CJB; j++) bdma16(rB, offb[j], soff, base + kBM * kSB + (RPWB * wave + 8 * j) * kSB);
   };
   // scales of stage pair p into scale slot SB: 16 B per row (2 copies per
   // wave with 4 waves, 1 with 8)
   auto issue_scales = [&](auto sb_tag, int p) {
-    uint8_t* sbase = w4_scales<decltype(sb_tag)::value>();
+    uint8_t* sbase = w4_scales<BN, decltype(sb_tag)::value>();
     const int pc = min(p, npairs - 1);
     if (NWV == 4) {
       dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
@@ -242,7 +253,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
     } else if (wave < 4) {
       dma16(gsa + (int64_t)pc * 16, sbase + (64 * wave) * 16);
     } else {
-      dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * (wave - 4)) * 16);
+      dma16(gsb + (int64_t)pc * 16, sbase + kBM * 16 + (64 * ((wave - 4) % (BN / 64))) * 16);
     }
   };
 
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   const int swz = (r32 >> 1) & 7;
   const int laneA = (wm * 128 + r32) * kSB, laneB = kBM * kSB + (wn * WCOLS + r32) * kSB;
   auto read_frag = [&](auto cb_tag, int kk, Frag& f) {
-    const uint8_t* ring = w4_codes<decltype(cb_tag)::value>();
+    const uint8_t* ring = w4_codes<BN, decltype(cb_tag)::value>();
     const int unit16 = ((kk * 2 + half) ^ swz) << 4;
     const uint8_t* pa = ring + laneA + unit16;
     const uint8_t* pb = ring + laneB + unit16;
@@ -280,7 +291,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   };
   // stage s's scale dwords: dwords 2(s&1), 2(s&1)+1 of the pair in slot SB
   auto read_scales = [&](auto sb_tag, int odd, Scales& sc) {
-    const unsigned* ss = (const unsigned*)w4_scales<decltype(sb_tag)::value>();
+    const unsigned* ss = (const unsigned*)w4_scales<BN, decltype(sb_tag)::value>();
     const int d0 = 2 * odd;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   issue_codes(C0{}, 0);
   issue_scales(C0{}, 0);
   issue_codes(C1{}, 1);
-  wait_vmcnt<2 * CJ>();  // stage 0 and the scales landed; stage 1 (2 CJ copies) may be in flight
+  wait_vmcnt<CJ + CJB>();  // stage 0 and the scales landed; stage 1 (CJ + CJB copies) may be in flight
   __builtin_amdgcn_s_barrier();
   read_scales(C0{}, 0, sc);
   read_frag(C0{}, 0, f0);
@@ -374,17 +385,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   if constexpr (OUT == kOutMx || OUT == kOutBf16) {
     // the bf16 tile into the two code slots (idle now that every wave has
     // read its last fragments): rows 0..127 in slot 0, 128..255 in slot 1,
-    // 512 bytes per row, 16-byte unit u of row r at u ^ (r & 31); then
+    // 2 BN bytes per row, 16-byte unit u of row r at u ^ (r % (BN / 8)); then
     // stored row by row in whole 16-byte units (bf16 output, a lane's own
     // 8-byte pieces wrote partial lines) or quantized (MXFP4 output)
     __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     __syncthreads();
-    uint8_t* lo = w4_codes<0>();
-    uint8_t* hi = w4_codes<1>();
+    constexpr int TROW = 2 * BN, TU = BN / 8;  // tile row bytes, 16-byte units per row
+    uint8_t* lo = w4_codes<BN, 0>();
+    uint8_t* hi = w4_codes<BN, 1>();
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int tr = wm * 128 + i * 32 + r32;
-      uint8_t* rowp = (tr < 128 ? lo : hi) + (tr & 127) * 512;
+      uint8_t* rowp = (tr < 128 ? lo : hi) + (tr & 127) * TROW;
 #pragma unroll
       for (int j = 0; j < JB; j++)
 #pragma unroll
@@ -392,14 +404,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
           const int tc = wn * WCOLS + j * 32 + q * 8 + 4 * half;
           const u32x2 o = {f32_to_bf16_rne(acc[i][j][4 * q]) | ((unsigned)f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16),
                            f32_to_bf16_rne(acc[i][j][4 * q + 2]) | ((unsigned)f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16)};
-          *(u32x2*)(rowp + (((tc >> 3) ^ (tr & 31)) << 4) + 2 * (tc & 7)) = o;
+          *(u32x2*)(rowp + (((tc >> 3) ^ (tr % TU)) << 4) + 2 * (tc & 7)) = o;
         }
     }
     __syncthreads();
     if constexpr (OUT == kOutMx)
-      store_mx_tile<256, 512>(lo, hi, m0, n0, m, n, (uint8_t*)c, cs);
+      store_mx_tile<256, TROW>(lo, hi, m0, n0, m, n, (uint8_t*)c, cs);
     else
-      store_bf16_tile<256, 512>(lo, hi, m0, n0, m, n, (uint16_t*)c);
+      store_bf16_tile<256, TROW>(lo, hi, m0, n0, m, n, (uint16_t*)c);
     return;
   }
 
@@ -440,6 +452,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
 #define MXQ_W4A4_RING_WAVES 8
 #endif
 constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
+// 256 x 128 tiles when 256 x 256 ones would fill at most half the CUs.
+// Measured on a 28672 x 8192 weight: m = 160-256 (112 wide tiles) 65-72 ->
+// 50-55 us; m = 384-512 (224 wide tiles) 68-76 us wide but 90-100 us narrow
+// (the narrow tile copies each A panel twice as often and reads more LDS per
+// MFMA).
+#ifndef MXQ_W4A4_NARROW_BELOW
+#define MXQ_W4A4_NARROW_BELOW 129
+#endif
 
 template <int OUT>
 static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
@@ -451,9 +471,19 @@ static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t*
   // the ring addresses its row panels with 32-bit offsets: 256 rows * k/2
   // bytes stay below 2^31 for k < 2^24
   if (k % 1024 == 0 && k >= 1024 && k < (1 << 24)) {
-    const unsigned tiles = (unsigned)(((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, OUT>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq, bs, m,
-                       n, k, c, cs);
+    const int64_t tm_n = (m + kBM - 1) / kBM;
+    // 256-column tiles unless they would leave most CUs idle: then
+    // 128-column tiles, twice as many
+    if constexpr (kRingWaves == 8) {
+      if (tm_n * ((n + 255) / 256) < MXQ_W4A4_NARROW_BELOW) {
+        const unsigned tiles = (unsigned)(tm_n * ((n + 127) / 128));
+        hipLaunchKernelGGL((k_w4a4_ring<8, OUT, 128>), dim3(tiles), dim3(512), 0, st, aq, as, bq, bs, m, n, k, c, cs);
+        return;
+      }
+    }
+    const unsigned tiles = (unsigned)(tm_n * ((n + 255) / 256));
+    hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, OUT, 256>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq,
+                       bs, m, n, k, c, cs);
     return;
   }
   dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));

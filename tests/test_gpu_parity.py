@@ -931,6 +931,32 @@ def test_w4a4_dynamic_full_size():
     say(f"w4a4 dynamic m=16: {len(cols)} sampled columns, worst |err|/S {worst:.3g}")
 
 
+# The ring takes 256 x 256 tiles only when they fill more than half the CUs
+# (at least 129 tiles); small test shapes take its 256 x 128 tiles.  Here
+# m and n are ragged against the 256 x 256 tile (2 x 129 tiles): sampled
+# outputs against the oracle, and the MXFP4 epilogue against quantize(gemm).
+def test_w4a4_wide_tile_ragged():
+    m, n, k = 300, 32900, 1024
+    rng = np.random.default_rng(77)
+    a = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 3).astype(np.float32))
+    qa, sa = oracle.mx_quantize(a)
+    qb, sb = oracle.mx_quantize(b)
+    rows = np.unique(np.concatenate([rng.choice(m, 24, replace=False), [0, 255, 256, m - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(n, 200, replace=False), [0, 255, 256, n - 257, n - 4, n - 1]]))
+    yref, S = oracle.gemm_nt(oracle.mx_dequantize(qa[rows], sa[rows]), oracle.mx_dequantize(qb[cols], sb[cols]))
+    args = (dev(qa), dev(sa), dev(qb), dev(sb))
+    for dt in (torch.float32, torch.bfloat16):
+        c = host(mxq.gemm_w4a4(*args, dt))
+        check_product(c[np.ix_(rows, cols)], yref, S, dt == torch.bfloat16, f"w4a4 wide tile {dt}")
+    n2 = 32928  # n % 32 == 0 for the MXFP4 output
+    qb2, sb2 = oracle.mx_quantize(synth.f32_to_bf16_bits((rng.standard_normal((n2, k)) * 3).astype(np.float32)))
+    qa_d, sa_d, qb_d, sb_d = dev(qa), dev(sa), dev(qb2), dev(sb2)
+    cq, cs = mxq.gemm_w4a4_quant(qa_d, sa_d, qb_d, sb_d)
+    q2, s2 = mxq.quantize(mxq.gemm_w4a4(qa_d, sa_d, qb_d, sb_d, torch.bfloat16))
+    assert torch.equal(cq, q2) and torch.equal(cs, s2), "wide tile: MXFP4 epilogue differs from quantize(gemm)"
+
+
 def test_w4a4_all_16x16_code_products_exact():
     """C[i][j] = E2M1(i) * E2M1(j) through the block-scaled MFMA (unit scales)."""
     k = 64
