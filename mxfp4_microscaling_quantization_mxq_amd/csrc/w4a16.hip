@@ -819,84 +819,99 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     a 28672 x 8192 weight).  The k order of a block's sum changes with
 //     its rotation; the result is still one fixed order per output row.
 //   * NVFP4: the tensor scale multiplies the fp32 sums in the epilogue.
-constexpr int kDdK = 512;             // k per stage
-constexpr int kDdRowB = kDdK / 2;     // code bytes per row per stage
-constexpr int kDdXRowB = kDdK * 2;    // activation bytes per row per stage
-template <bool kNv>
-constexpr int dd_scale_bytes() { return kNv ? kDdK / 16 : kDdK / 32; }  // per row per stage
-
+// Stage geometry of the decode ring for KS k per stage (512 or 256).
+template <int KS, bool kNv>
+struct DdGeom {
+  static constexpr int RowB = KS / 2;                 // code bytes per weight row
+  static constexpr int U = RowB / 16;                 // 16-byte units per weight row (16 or 8)
+  static constexpr int RPI = 64 / U;                  // weight rows per 1-KiB copy (4 or 8)
+  static constexpr int WC = 16 / RPI;                 // weight copies per wave (16 rows)
+  static constexpr int XRowB = 2 * KS;                // bf16 activation bytes per row
+  static constexpr int XRPI = 1024 / XRowB;           // activation rows per 1-KiB copy (1 or 2)
+  static constexpr int ScB = kNv ? KS / 16 : KS / 32;  // scale bytes per weight row (8 .. 32)
+  // scales sit in 256-byte pieces, 16 bytes per row per piece; a row with 8
+  // scale bytes fills the first half of its 16 (the copy repeats them)
+  static constexpr int SCP = ScB > 16 ? ScB / 16 : 1;  // scale pieces (copies) per wave
+  static constexpr int SPL = ScB < 16 ? ScB / 4 : 4;   // distinct 4-byte parts per row and piece
+  static constexpr int STEPS = KS / 128;              // 128-k chunks (4 per lane group) per stage
+};
 
 // One ring slot: codes, activations and scales of one stage.  Every slot is
 // its own LDS variable and every slot index below is a compile-time
 // constant, so the compiler can tell that the reads of slot b do not touch
 // the slots whose copies are still in flight (one shared array would make it
 // wait for every outstanding copy before the first read).
-template <int MT, int NW, bool kNv>
+template <int MT, int NW, int KS, bool kNv>
 struct DdSlot {
-  uint8_t w[16 * NW * kDdRowB];
-  uint8_t x[(MT + 2) * kDdXRowB];  // MT activation rows, a zero row, a scratch row
-  uint8_t s[16 * NW * dd_scale_bytes<kNv>()];
+  using G = DdGeom<KS, kNv>;
+  uint8_t w[16 * NW * G::RowB];
+  uint8_t x[(MT + 1 + G::XRPI) * G::XRowB];  // MT activation rows, a zero row, scratch rows
+  uint8_t s[NW * G::SCP * 256];
 };
-template <int MT, int NW, bool kNv, int B>
-__device__ __forceinline__ DdSlot<MT, NW, kNv>& dd_slot() {
-  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW, kNv> slot;
+template <int MT, int NW, int KS, bool kNv, int B>
+__device__ __forceinline__ DdSlot<MT, NW, KS, kNv>& dd_slot() {
+  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW, KS, kNv> slot;
   return slot;
 }
 
-template <bool kNv, int MT, int NW, int NR, bool kBf16Out>
+template <bool kNv, int MT, int NW, int NR, int KS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* __restrict__ wq,
                                                                 const uint8_t* __restrict__ ws,
                                                                 const float* __restrict__ gscale, int64_t n,
                                                                 int64_t k, const uint16_t* __restrict__ x,
                                                                 int64_t m, void* __restrict__ y) {
-  using Slot = DdSlot<MT, NW, kNv>;
-  constexpr int ScB = dd_scale_bytes<kNv>();  // scale bytes per row per stage (16 or 32)
-  constexpr int SCP = ScB / 16;               // scale copies per wave (16 rows x 16 B each)
-  constexpr int RB = 16 * NW;                 // weight rows per block
-  constexpr int XPW = (MT + NW - 1) / NW;     // activation-row copies per wave per stage
-  constexpr int D = 4 + SCP + XPW;            // copies per wave per stage
-  static_assert(NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "ring depth / vmcnt range");
+  using G = DdGeom<KS, kNv>;
+  using Slot = DdSlot<MT, NW, KS, kNv>;
+  constexpr int RB = 16 * NW;                          // weight rows per block
+  constexpr int MTT = (MT + 15) / 16;                  // 16-row activation tiles
+  constexpr int XPW = (MT / G::XRPI + NW - 1) / NW;    // activation copies per wave per stage
+  constexpr int D = G::WC + G::SCP + XPW;              // copies per wave per stage
+  static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
-  const int nst = (int)(k / kDdK);
-  const int rot = (int)((blockIdx.x / 8) % (unsigned)nst);
+  const int nst = (int)(k / KS);
+  // staggered start, counted in 512-k chunks (the same k order for either
+  // stage length)
+  const int rot = (int)((blockIdx.x / 8) % (unsigned)(k / 512)) * (512 / KS);
 
-  // zero rows (activation rows m..15 of the MFMA operand read them)
-  for (int i = tid; i < kDdXRowB / 16; i += 64 * NW) {
+  // zero row (activation rows m..MT-1 of the MFMA operand read it)
+  for (int i = tid; i < G::XRowB / 16; i += 64 * NW) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(dd_slot<MT, NW, kNv, 0>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, kNv, 1 % NR>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, kNv, 2 % NR>().x + MT * kDdXRowB + 16 * i) = z;
-    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, kNv, 3 % NR>().x + MT * kDdXRowB + 16 * i) = z;
+    *(u32x4*)(dd_slot<MT, NW, KS, kNv, 0>().x + MT * G::XRowB + 16 * i) = z;
+    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 1 % NR>().x + MT * G::XRowB + 16 * i) = z;
+    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 2 % NR>().x + MT * G::XRowB + 16 * i) = z;
+    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 3 % NR>().x + MT * G::XRowB + 16 * i) = z;
   }
   __syncthreads();
 
-  // copies of stage s into ring slot B: 4 code instructions, 1 scale
-  // instruction, XPW activation instructions.  A stage past the end is
-  // clamped to the last one (a re-read from L2 into a slot nobody reads), so
-  // every step issues the same copies and waits for the same count, and the
-  // code between the copies and the reads has no branch.  Lane offsets are
-  // fixed for the whole k loop; a stage only moves the uniform bases.
-  unsigned offw[4], offx[XPW];
+  // Copies of stage s into ring slot B.  A stage past the end is clamped to
+  // the last one (a re-read from L2 into a slot nobody reads), so every step
+  // issues the same copies and waits for the same count, and the code
+  // between the copies and the reads has no branch.  Lane offsets are fixed
+  // for the whole k loop; a stage only moves the uniform offset.
+  unsigned offw[G::WC], offx[XPW];
   int xdst[XPW];
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int row = 16 * wave + 4 * q + (lane >> 4);  // block row of this lane
-    const unsigned unit = (unsigned)((lane & 15) ^ (row & 15));
+  for (int q = 0; q < G::WC; q++) {
+    const int row = 16 * wave + G::RPI * q + lane / G::U;  // block row of this lane
+    const unsigned unit = (unsigned)((lane % G::U) ^ (row % G::U));
     offw[q] = (unsigned)min(row, rows_w - 1) * (unsigned)kq + (unit << 4);
   }
-  // scale copy h covers 64 lanes x 4 B = 16 B of each of the wave's 16
-  // rows: lane i takes row i / 4, bytes 16 h + 4 (i % 4) .. +4
-  const unsigned offs = (unsigned)min(16 * wave + (lane >> 2), rows_w - 1) * (unsigned)ks + 4u * (lane & 3);
+  // scale copy h: lane i takes row i / 4 of the wave, 4 bytes at 16 h +
+  // 4 ((i % 4) % SPL) of the row's stage bytes
+  const unsigned offs = (unsigned)min(16 * wave + (lane >> 2), rows_w - 1) * (unsigned)ks +
+                        4u * (unsigned)((lane & 3) % G::SPL);
 #pragma unroll
   for (int j = 0; j < XPW; j++) {
-    const int xr = wave + NW * j;  // activation row of this copy (wave-uniform)
-    const bool real = xr < m;
-    offx[j] = real ? (unsigned)xr * (unsigned)kx + ((unsigned)(lane ^ (xr & 15)) << 4) : 0u;
-    xdst[j] = (real ? xr : MT + 1) * kDdXRowB;
+    const int a = wave + NW * j;  // copy slot (wave-uniform): activation rows XRPI a ..
+    const int xr = G::XRPI * a + lane / (64 / G::XRPI);
+    const bool real = G::XRPI * a < MT;
+    const unsigned unit = (unsigned)((lane % (64 / G::XRPI)) ^ (xr & 15));
+    offx[j] = (unsigned)min((int64_t)xr, m - 1) * (unsigned)kx + (unit << 4);
+    xdst[j] = (real ? G::XRPI * a : MT + 1) * G::XRowB;
   }
   // buffer resources over the block's weight, scale and activation panels
   // (32-bit lane offsets; the panels stay below 2^31 bytes for k <= 2^24)
@@ -905,37 +920,38 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   const __amdgpu_buffer_rsrc_t rx = panel_rsrc(x, m * kx);
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    Slot& sl = dd_slot<MT, NW, kNv, B>();
+    Slot& sl = dd_slot<MT, NW, KS, kNv, B>();
     const int sl0 = min(s, nst - 1);
     const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
-    for (int q = 0; q < 4; q++) bdma16(rw, offw[q], sc * kDdRowB, sl.w + (16 * wave + 4 * q) * kDdRowB);
-    // LDS: scale piece h of the wave's rows at s + (SCP wave + h) * 256,
-    // row r of the wave at + 16 r (so row r's bytes 16 h.. sit in piece h)
+    for (int q = 0; q < G::WC; q++)
+      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+    // LDS: piece h of the wave's rows at s + (SCP wave + h) * 256, row r of
+    // the wave at + 16 r
 #pragma unroll
-    for (int h = 0; h < SCP; h++) bdma4(rs, offs + 16u * h, sc * ScB, sl.s + (SCP * wave + h) * 256);
+    for (int h = 0; h < G::SCP; h++) bdma4(rs, offs + 16u * h, sc * G::ScB, sl.s + (G::SCP * wave + h) * 256);
 #pragma unroll
-    for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * kDdXRowB, sl.x + xdst[j]);
+    for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + xdst[j]);
   };
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MTT];
+#pragma unroll
+  for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int wrow = 16 * wave + col;  // this lane's block weight row
-  const bool xreal = col < m;
   auto compute = [&](auto slot_tag) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = dd_slot<MT, NW, kNv, B>();
-    const uint8_t* xb = sl.x + (xreal ? col : MT) * kDdXRowB;
-    const int xsw = xreal ? col : 0;
-    // this lane's row's scale bytes: 16 (E8M0 per 32 k) or 32 (E4M3 per 16)
-    unsigned svs[ScB / 4];
+    const Slot& sl = dd_slot<MT, NW, KS, kNv, B>();
+    // this lane's row's scale bytes of the stage: ScB (E8M0 per 32 k or
+    // E4M3 per 16), word w = bytes 4w .. 4w+3
+    unsigned svs[G::SCP * 4];
 #pragma unroll
-    for (int h = 0; h < SCP; h++) {
-      const u32x4 sv = *(const u32x4*)(sl.s + (SCP * wave + h) * 256 + 16 * col);
+    for (int h = 0; h < G::SCP; h++) {
+      const u32x4 sv = *(const u32x4*)(sl.s + (G::SCP * wave + h) * 256 + 16 * col);
       svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u32x4 cw = *(const u32x4*)(sl.w + wrow * kDdRowB + (((4 * i + g) ^ col) << 4));
+    for (int i = 0; i < G::STEPS; i++) {
+      const u32x4 cw = *(const u32x4*)(sl.w + wrow * G::RowB + (((4 * i + g) ^ (col % G::U)) << 4));
       bf16x8 wf[4];
       if constexpr (kNv) {
         // the two E4M3 scales of chunk 4i + g: bytes 8i + 2g, 8i + 2g + 1
@@ -944,9 +960,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
         dequant_chunk<false>(cw, (svs[i] >> (8 * g)) & 0xFFu, wf);
       }
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const bf16x8 xa = *(const bf16x8*)(xb + ((16 * i + ((4 * g + j) ^ xsw)) << 4));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wf[j], acc, 0, 0, 0);
+      for (int t = 0; t < MTT; t++) {
+        const int xr = 16 * t + col;
+        const bool xreal = xr < m;
+        const uint8_t* xb = sl.x + (xreal ? xr : MT) * G::XRowB;
+        const int xsw = xreal ? (xr & 15) : 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const bf16x8 xa = *(const bf16x8*)(xb + ((16 * i + ((4 * g + j) ^ xsw)) << 4));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wf[j], acc[t], 0, 0, 0);
+        }
       }
     }
   };
@@ -985,34 +1008,58 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   }
   wait_vmcnt<0>();
 
-  // lane holds y[4g + i][n0 + wrow]
+  // lane holds y[16t + 4g + i][n0 + wrow]
   const float st = kNv ? *gscale : 1.0f;
   const int64_t nn = n0 + wrow;
   if (nn < n) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t mm = 4 * g + i;
-      if (mm >= m) continue;
-      const float o = kNv ? acc[i] * st : acc[i];
-      if (kBf16Out)
-        ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(o);
-      else
-        ((float*)y)[mm * n + nn] = o;
-    }
+    for (int t = 0; t < MTT; t++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int64_t mm = 16 * t + 4 * g + i;
+        if (mm >= m) continue;
+        const float o = kNv ? acc[t][i] * st : acc[t][i];
+        if (kBf16Out)
+          ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(o);
+        else
+          ((float*)y)[mm * n + nn] = o;
+      }
   }
 }
 
-template <bool kNv, int MT, int NW, int NR>
+template <bool kNv, int MT, int NW, int NR, int KS>
 static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                               const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, true>), grid, dim3(64 * NW), 0, st, wq, ws, gscale, n,
-                       k, (const uint16_t*)x, m, y);
-  else
-    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, false>), grid, dim3(64 * NW), 0, st, wq, ws, gscale,
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, wq, ws, gscale,
                        n, k, (const uint16_t*)x, m, y);
+  else
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, wq, ws,
+                       gscale, n, k, (const uint16_t*)x, m, y);
 }
+
+// Decode ring configurations <MT, NW, NR, KS> by activation rows.
+#ifndef MXQ_DD_KS32
+#define MXQ_DD_KS32 256
+#define MXQ_DD_NR32 4
+#endif
+template <bool kNv>
+static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
+                               const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
+  if (m <= 4)
+    launch_decode_dma<kNv, 4, 7, 3, 512>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  else if (m <= 16)
+    launch_decode_dma<kNv, 16, 7, 3, 512>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  else if (m <= 32)
+    launch_decode_dma<kNv, 32, 7, MXQ_DD_NR32, MXQ_DD_KS32>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  else
+    launch_decode_dma<kNv, 64, 7, 3, 256>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+}
+
+#ifndef MXQ_DD_MAXM
+#define MXQ_DD_MAXM 64
+#endif
 
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
@@ -1020,13 +1067,20 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
   // costs vector-ALU work per weight element in the ring, while the
   // vector-ALU kernel applies each E4M3 scale once per 16 products (measured
   // on 28672 x 8192: m = 2 29.5 vs 40-45 us, m = 4 47-50 vs 39-41 us).
-  if (m >= (nv ? 4 : 2) && m <= 16 && k % kDdK == 0 && k <= (1 << 24) && n >= 16 * 7 * 128) {
-    if (m <= 4)
-      nv ? launch_decode_dma<true, 4, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
-         : launch_decode_dma<false, 4, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
-    else
-      nv ? launch_decode_dma<true, 16, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
-         : launch_decode_dma<false, 16, 7, 3>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  const bool ring = k % 512 == 0 && k <= (1 << 24) && n >= 16 * 7 * 128;
+  // m = MAXM+1 .. 2 MAXM in two passes, the first over MAXM activation rows
+  // on the ring, the second over the rest by this same dispatch: two reads of
+  // the weight cost less than the tiled GEMM at these heights (28672 x 8192:
+  // about 2 x 60 us against 156 us for the GEMM at m = 128).
+  if (ring && m > MXQ_DD_MAXM && m <= 2 * MXQ_DD_MAXM) {
+    const hipError_t e = launch_w4a16(nv, wq, ws, gscale, n, k, x, MXQ_DD_MAXM, y, bf16_out, st);
+    if (e != hipSuccess) return e;
+    return launch_w4a16(nv, wq, ws, gscale, n, k, (const uint16_t*)x + MXQ_DD_MAXM * k, m - MXQ_DD_MAXM,
+                        (uint8_t*)y + MXQ_DD_MAXM * n * (bf16_out ? 2 : 4), bf16_out, st);
+  }
+  if (ring && m >= (nv ? 4 : 2) && m <= MXQ_DD_MAXM) {
+    nv ? launch_decode_ring<true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
+       : launch_decode_ring<false>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (!nv && m >= 5 && m <= 16) {
     const dim3 grid((unsigned)((n + 63) / 64));
     if (bf16_out)

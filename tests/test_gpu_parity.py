@@ -586,11 +586,16 @@ def test_gemv_ragged_shapes(n, k, m):
 
 
 # Shapes that reach the DMA-fed decode kernel (n >= 14336 rows, k a
-# multiple of 512, 2 <= m <= 16): one to eight 512-k stages against a three-
-# or four-slot ring, row tails that leave part of the last block empty, and
-# activation counts on both sides of the 4-row variant.
+# multiple of 512, 2 <= m <= 64): one to eight 512-k stages against a three-
+# slot ring (4- and 16-row activation tiles), two to sixteen 256-k stages
+# against a four-slot ring (32-row tiles) and a three-slot ring (64-row
+# tiles), row tails that leave part of the last block empty, and activation
+# counts on both sides of every tile height; m = 65..128 runs as a 64-row pass
+# plus a pass over the rest.
 @pytest.mark.parametrize("n,k,m", [(14336, 512, 2), (14373, 1024, 3), (14447, 1536, 4), (14400, 2048, 5),
-                                   (14336, 2560, 16), (15000, 1536, 12), (14336, 4096, 2)])
+                                   (14336, 2560, 16), (15000, 1536, 12), (14336, 4096, 2), (14336, 512, 17),
+                                   (14373, 1536, 32), (14400, 4096, 33), (14447, 1024, 48), (14336, 2560, 64),
+                                   (15000, 512, 64), (14336, 1024, 65), (14373, 1536, 100), (14400, 512, 128)])
 def test_gemv_decode_dma_shapes(n, k, m):
     w = laplace_bf16(n + 7 * k + m, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(100 + m).standard_normal((m, k)).astype(np.float32))
@@ -633,7 +638,7 @@ def decode_weight():
     return w, qo, so
 
 
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16, 32, 64, 100])
 def test_gemv_decode_full_size_sampled(m):
     w, qo, so = decode_weight()
     if m == 1:
@@ -670,10 +675,13 @@ def test_nv_gemm_ragged():
 
 # NVFP4 weights at decode sizes: the staged-scale path of the m <= 4 kernel
 # (k % 256 == 0, whole 2048-k ranges; a partial last range and k % 32 == 16
-# take the byte-wise path), and the m = 2..16 ring kernel (n >= 14336,
-# k % 512 == 0) with ragged weight rows.
+# take the byte-wise path), and the m = 4..64 ring kernel (n >= 14336,
+# k % 512 == 0; 512-k stages up to 16 rows, 256-k stages above; two passes
+# for m = 65..128) with ragged weight rows.
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
-                                   (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16)])
+                                   (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16), (14373, 512, 17),
+                                   (14400, 1536, 32), (14336, 2560, 40), (14447, 1024, 64),
+                                   (14373, 512, 66), (14400, 1024, 128)])
 def test_nv_decode_paths(n, k, m):
     w = laplace_bf16(n + 3 * k + m, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(k + m).standard_normal((m, k)).astype(np.float32))
@@ -693,9 +701,9 @@ def decode_weight_nv():
     return oracle.nv_quantize(w)
 
 
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16, 32, 64, 100])
 def test_nv_decode_full_size_sampled(m):
-    """The 28672 x 8192 decode weight in NVFP4 at m = 1, 4, 16."""
+    """The 28672 x 8192 decode weight in NVFP4 at m = 1, 4, 16, 32, 64, 100."""
     qo, so, go = decode_weight_nv()
     _, x = synth.decode_gemv(m)
     n = qo.shape[0]
