@@ -1053,6 +1053,8 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
     launch_decode_dma<kNv, 16, 7, 3, 512>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 32)
     launch_decode_dma<kNv, 32, 7, MXQ_DD_NR32, MXQ_DD_KS32>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  else if (m <= 48)
+    launch_decode_dma<kNv, 48, 7, 3, 256>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else
     launch_decode_dma<kNv, 64, 7, 3, 256>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
 }
