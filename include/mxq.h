@@ -150,8 +150,10 @@ MXQ_API mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *s, int64_t ro
  * written out in 16 bits), x[m][k] is bf16, accumulation is fp32, and y is
  * written as ydt (MXQ_F32 or MXQ_BF16, round to nearest even).  Weight-only
  * 4-bit with 16-bit multiplies saves bandwidth, not arithmetic
- * [infra-guide sec. 4.2 and 5].  Any m >= 1: m <= 16 takes the memory-bound
- * decode (GEMV) kernel, larger m a bf16-MFMA GEMM tile.  k % 32 == 0.
+ * [infra-guide sec. 4.2 and 5].  Any m >= 1.  Memory-bound decode kernels
+ * up to m = 127; for n >= 14336 and k % 512 == 0 a weight-streaming ring of
+ * up to 64 activation rows, with m = 65..128 as two launches of it.  Larger
+ * m takes a bf16-MFMA GEMM tile.  k % 32 == 0.
  */
 MXQ_API mxq_status mxq_gemv_w4a16(const uint8_t *wq, const uint8_t *ws, int64_t n,
                           int64_t k, const void *x, int64_t m, void *y,
