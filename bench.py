@@ -1,6 +1,7 @@
 """Benchmark of the MXFP4 / NVFP4 hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only parts] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--singles N] [--only parts] [--ops names]
+                [--no-cpu-baseline] [--no-ceilings] [--no-metrics]
 
 One step runs every row of the hot path once, on seeded synthetic inputs
 already resident in HBM:
@@ -10,9 +11,9 @@ already resident in HBM:
          TransFP4 block quantize (rotation, bf16 residual, NVFP4/INT4 choice)
          of the same tensor and its dequantization
   gemv   W4A16 decode GEMV, MXFP4 weight 28672x8192, bf16 x at m = 1, 4, 16
-         (and the same weight in NVFP4 at m = 1, 16);
-         on the same weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x), and
-         both from bf16 x quantized inside the GEMM (the small-m kernel)
+         (and 64; the same weight in NVFP4 at m = 1, 16, 64); on the same
+         weight at m = 16: W4A4 (MXFP4 x), W4A8 (MXFP8 x), and both from bf16
+         x quantized inside the GEMM (the small-m kernel)
   w4a4   MXFP4 quantize of A 8192x8192 + W4A4 GEMM 8192^3 on block-scaled MFMA
          (bf16 output, and MXFP4 output quantized in the epilogue); MXFP8
          quantize of the same A + W4A8 GEMM 8192^3 (E4M3 x E2M1 MFMA)
@@ -21,17 +22,29 @@ already resident in HBM:
 Every HBM-bound op cycles through copies of its operands whose combined size
 exceeds the 256 MB Infinity Cache, so each launch streams from HBM.
 
-Timing, all with HIP events on the stream the library launches on (torch's
-current stream): K timed steps (ms_per_step = wall time / K; each call also
-bracketed by its own event pair), then per op a kernel-rate region of BURST
-back-to-back launches per event pair, whose per-launch average is the
-kernel's duration used for GB/s, TFLOP/s and the roofline fractions.  The
-JSON line's value is the decode GEMV's achieved HBM bandwidth at m = 1
-(algorithmic bytes / that duration); the W4A4 GEMM TFLOP/s is beside it.
+Timing, with HIP events on the stream the library launches on (torch's
+current stream):
+  1. K timed steps of the whole path, bracketed by a synchronize on both
+     sides: ms_per_step.
+  2. Per op, N (default 50) launches queued back to back, each between its
+     own event pair: the median is the op's single-launch duration (an event
+     pair adds the time the command processor takes to retire the marker
+     packets around one launch, a few microseconds).
+  3. Per op, bursts of 16 back-to-back launches between one event pair: the
+     per-launch average is the kernel's steady-state duration.  The roofline
+     figures (GB/s, TFLOP/s, fractions of the datasheet peak and of the
+     measured ceiling) use it; both durations are in the JSON line.
+The on-box ceilings (a pure streaming read of the decode weight's size, the
+fp4 and bf16 MFMA issue rates with the shader clock they ran at) come from
+the measurement kernels in libmxq_ceiling.so.  After timing, the quality
+metrics (NMSE, cosine; host, float64) of the tiny reference and of the
+NVFP4-vs-MXFP4 tensors and products are computed from the GPU's outputs.
+The JSON line's value is the decode GEMV's achieved HBM bandwidth at m = 1.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -46,10 +59,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0
 FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA; an E4M3 x E2M1 product issues at this rate
-BURST = 16  # launches per event pair in the kernel-rate region
-COLD_BYTES = 768 << 20  # rotation set size for HBM-bound ops (3x the 256 MB cache)
 BF16_PEAK_TFLOPS = 2500.0
+PEAKS = {"hbm": HBM_PEAK_GBS, "fp4": FP4_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS}
+BURST = 16  # launches per event pair in the burst region
+COLD_BYTES = 768 << 20  # rotation set size for HBM-bound ops (3x the 256 MB cache)
 METRIC = "MXFP4 W4A16 GEMV HBM GB/s (% peak); W4A4 GEMM TFLOPS (% MXFP4 MFMA peak)"
+HEAD = "gemv_w4a16_m1"
 
 
 def parse():
@@ -57,10 +72,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--singles", type=int, default=50, help="single launches per op (median)")
+    p.add_argument("--bursts", type=int, default=5, help="bursts of 16 launches per op (median)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true")
+    p.add_argument("--no-metrics", action="store_true")
     p.add_argument("--only", default="",
                    help="comma list of parts to run (tiny,quant,gemv,w4a4,c5; 'copy' adds a 1 GiB device copy "
                         "used to calibrate HBM byte counters)")
+    p.add_argument("--ops", default="", help="comma list of op-name prefixes to time (default: all)")
     return p.parse_args()
 
 
@@ -108,7 +128,8 @@ def main():
 
     t_gen = time.time()
     print("generating inputs ...", file=sys.stderr, flush=True)
-    ops = []  # (name, callable, bytes, flops)
+    ops = []  # (name, callable, bytes, flops, bound)
+    keep = {}  # GPU tensors the quality metrics read after timing
     bf16 = torch.bfloat16
     u8 = torch.uint8
 
@@ -134,21 +155,23 @@ def main():
         s1 = torch.empty((256, 16), dtype=u8, device=dev)
         y1 = torch.empty((256, 512), dtype=torch.float32, device=dev)
         g1 = torch.empty((1, 256), dtype=bf16, device=dev)
-        ops.append(("tiny_quantize_f32", lambda: mxq.quantize(w1d, q1, s1), quant_bytes(256, 512, 4), 0))
+        ops.append(("tiny_quantize_f32", lambda: mxq.quantize(w1d, q1, s1), quant_bytes(256, 512, 4), 0, "hbm"))
         ops.append(("tiny_dequantize_f32", lambda: mxq.dequantize(q1, s1, y=y1),
-                    mx_bytes(256, 512) + 256 * 512 * 4, 0))
+                    mx_bytes(256, 512) + 256 * 512 * 4, 0, "hbm"))
         ops.append(("tiny_gemv_m1", lambda: mxq.gemv_w4a16(q1, s1, x1d, y=g1), gemv_bytes(256, 512, 1),
-                    2 * 256 * 512))
+                    2 * 256 * 512, "hbm"))
+        keep["tiny"] = (w1, x1, y1, g1)
     if "quant" in parts:
         x3 = to_dev(synth.dynamic_quantize())
         n3 = ncopies(quant_bytes(16384, 8192))
         sets = [(x3 if c == 0 else x3.clone(), torch.empty((16384, 4096), dtype=u8, device=dev),
                  torch.empty((16384, 256), dtype=u8, device=dev)) for c in range(n3)]
         ops.append(("quantize_16384x8192_bf16", rotating(sets, lambda x, q, s: mxq.quantize(x, q, s)),
-                    quant_bytes(16384, 8192), 0))
+                    quant_bytes(16384, 8192), 0, "hbm"))
         # rotated MXFP4 (32-point block Hadamard fused ahead of the quantizer)
         ops.append(("quantize_hadamard32_16384x8192_bf16",
-                    rotating(sets, lambda x, q, s: mxq.quantize_hadamard(x, 32, q, s)), quant_bytes(16384, 8192), 0))
+                    rotating(sets, lambda x, q, s: mxq.quantize_hadamard(x, 32, q, s)), quant_bytes(16384, 8192), 0,
+                    "hbm"))
         # TransFP4 blocks: tensor-scale pass + quantize pass (x read twice),
         # then the dequantization back to bf16
         ntf = 16384 * 8192
@@ -158,14 +181,14 @@ def main():
         tf4_bytes = ntf // 2 + ntf // 16 + ntf // 32 + ntf // 16  # codes, E4M3, meta, bf16 residual
         ops.append(("transfp4_quantize_16384x8192_bf16",
                     rotating(tsets, lambda x, q, s, m, r, g: mxq.transfp4_quantize(x, None, q, s, m, r, g)),
-                    2 * 2 * ntf + tf4_bytes, 0))
+                    2 * 2 * ntf + tf4_bytes, 0, "hbm"))
         ydq = [torch.empty((16384, 8192), dtype=bf16, device=dev) for _ in tsets]
         for (x, q, s_, m, r, g) in tsets:
             mxq.transfp4_quantize(x, None, q, s_, m, r, g)
         ops.append(("transfp4_dequantize_16384x8192_bf16",
                     rotating([(q, s_, m, r, g, y) for (x, q, s_, m, r, g), y in zip(tsets, ydq)],
                              lambda q, s_, m, r, g, y: mxq.transfp4_dequantize(q, s_, m, r, g, y=y)),
-                    tf4_bytes + 2 * ntf, 0))
+                    tf4_bytes + 2 * ntf, 0, "hbm"))
     if "gemv" in parts:
         n2, k2 = 28672, 8192
         w2, _ = synth.decode_gemv(1)
@@ -179,7 +202,7 @@ def main():
             ym = torch.empty((m, n2), dtype=bf16, device=dev)
             ops.append((f"gemv_w4a16_m{m}",
                         rotating([(q, s, xm, ym) for q, s in copies], lambda q, s, x, y: mxq.gemv_w4a16(q, s, x, y=y)),
-                        gemv_bytes(n2, k2, m), 2 * m * n2 * k2))
+                        gemv_bytes(n2, k2, m), 2 * m * n2 * k2, "hbm"))
         # the same weight in NVFP4 (E4M3 per 16 + fp32 tensor scale)
         qn2, sn2, gn2 = mxq.nv_quantize(to_dev(w2))
         del w2
@@ -191,7 +214,7 @@ def main():
             ops.append((f"nv_gemv_w4a16_m{m}",
                         rotating([(q, s) for q, s in ncopies_nv],
                                  lambda q, s, x=xm, y=ym: mxq.nv_gemm(q, s, gn2, x, y=y)),
-                        nv_bytes(n2, k2) + m * k2 * 2 + m * n2 * 2, 2 * m * n2 * k2))
+                        nv_bytes(n2, k2) + m * k2 * 2 + m * n2 * 2, 2 * m * n2 * k2, "hbm"))
         # decode-sized W4A4 / W4A8 on the same weight (the small-m kernel:
         # the weight stream bounds it), and W4A4 straight from bf16
         # activations with their quantization fused into the GEMM
@@ -202,16 +225,16 @@ def main():
         out16 = 16 * n2 * 2
         ops.append(("decode_w4a4_m16", rotating([(q, s) for q, s in copies],
                                                 lambda q, s: mxq.gemm_w4a4(qx16, sx16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + mx_bytes(16, k2) + out16, 2 * 16 * n2 * k2))
+                    mx_bytes(n2, k2) + mx_bytes(16, k2) + out16, 2 * 16 * n2 * k2, "hbm"))
         ops.append(("decode_w4a8_m16", rotating([(q, s) for q, s in copies],
                                                 lambda q, s: mxq.gemm_w4a8(qx8, sx8, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2))
+                    mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2, "hbm"))
         ops.append(("decode_w4a4_dynamic_m16", rotating([(q, s) for q, s in copies],
                                                         lambda q, s: mxq.gemm_w4a4_dynamic(x16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2))
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm"))
         ops.append(("decode_w4a8_dynamic_m16", rotating([(q, s) for q, s in copies],
                                                         lambda q, s: mxq.gemm_w4a8_dynamic(x16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2))
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm"))
     if "w4a4" in parts:
         a4, b4 = synth.w4a4_operands()
         a4d = to_dev(a4)
@@ -224,30 +247,29 @@ def main():
         sets = [(a4d if c == 0 else a4d.clone(), qa4 if c == 0 else torch.empty_like(qa4),
                  sa4 if c == 0 else torch.empty_like(sa4)) for c in range(na)]
         ops.append(("quantize_a_8192x8192_bf16", rotating(sets, lambda x, q, s: mxq.quantize(x, q, s)),
-                    quant_bytes(8192, 8192), 0))
+                    quant_bytes(8192, 8192), 0, "hbm"))
         # the GEMM is compute-bound (its 68 MB of operands may stay in the cache)
         ops.append(("gemm_w4a4_8192", lambda: mxq.gemm_w4a4(qa4, sa4, qb4, sb4, c=c4),
-                    2 * mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3))
+                    2 * mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3, "fp4"))
         # the same product with the MXFP4 quantization of its output fused
         # into the epilogue (the next layer's activations, no bf16 round trip)
         cq4 = torch.empty((8192, 4096), dtype=u8, device=dev)
         cs4 = torch.empty((8192, 256), dtype=u8, device=dev)
         ops.append(("gemm_w4a4_8192_mxfp4_out", lambda: mxq.gemm_w4a4_quant(qa4, sa4, qb4, sb4, cq4, cs4),
-                    3 * mx_bytes(8192, 8192), 2 * 8192 ** 3))
+                    3 * mx_bytes(8192, 8192), 2 * 8192 ** 3, "fp4"))
         # MXFP8 activations (E4M3 + E8M0 per 32) against the same MXFP4 weights
         qa8 = torch.empty((8192, 8192), dtype=u8, device=dev)
         sa8 = torch.empty((8192, 256), dtype=u8, device=dev)
         sets8 = [(a4d if c == 0 else sets[c][0], qa8 if c == 0 else torch.empty_like(qa8),
                   sa8 if c == 0 else torch.empty_like(sa8)) for c in range(na)]
         ops.append(("quantize_fp8_a_8192x8192_bf16", rotating(sets8, lambda x, q, s: mxq.quantize_fp8(x, q, s)),
-                    8192 * 8192 * 3 + 8192 * 256, 0))
+                    8192 * 8192 * 3 + 8192 * 256, 0, "hbm"))
         ops.append(("gemm_w4a8_8192", lambda: mxq.gemm_w4a8(qa8, sa8, qb4, sb4, c=c4),
-                    8192 * 8192 + 8192 * 256 + mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3))
+                    8192 * 8192 + 8192 * 256 + mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3, "fp8"))
     if "c5" in parts:
         w5, x5 = synth.nv_vs_mx()
         w5d, x5d = to_dev(w5), to_dev(x5)
         n5, k5, m5 = 8192, 4096, 4096
-        del w5, x5
 
         def qsets(src, rows, blk):
             nb = ncopies(rows * k5 * 2 + rows * k5 // 2 + rows * k5 // blk)
@@ -262,62 +284,67 @@ def main():
 
         def mxqz(x, q, s, g):
             mxq.quantize(x, q, s)
-        ops.append(("nv_quantize_w_8192x4096", rotating(nvw, nvq), n5 * k5 * 2 * 2 + nv_bytes(n5, k5), 0))
-        ops.append(("nv_quantize_x_4096x4096", rotating(nvx, nvq), m5 * k5 * 2 * 2 + nv_bytes(m5, k5), 0))
-        ops.append(("mx_quantize_w_8192x4096", rotating(mxw, mxqz), quant_bytes(n5, k5), 0))
-        ops.append(("mx_quantize_x_4096x4096", rotating(mxx, mxqz), quant_bytes(m5, k5), 0))
+        ops.append(("nv_quantize_w_8192x4096", rotating(nvw, nvq), n5 * k5 * 2 * 2 + nv_bytes(n5, k5), 0, "hbm"))
+        ops.append(("nv_quantize_x_4096x4096", rotating(nvx, nvq), m5 * k5 * 2 * 2 + nv_bytes(m5, k5), 0, "hbm"))
+        ops.append(("mx_quantize_w_8192x4096", rotating(mxw, mxqz), quant_bytes(n5, k5), 0, "hbm"))
+        ops.append(("mx_quantize_x_4096x4096", rotating(mxx, mxqz), quant_bytes(m5, k5), 0, "hbm"))
         y5n = torch.empty((m5, n5), dtype=bf16, device=dev)
         y5m = torch.empty((m5, n5), dtype=bf16, device=dev)
         _, wnq, wns, wng = nvw[0]
         _, wmq, wms, _ = mxw[0]
         mxq.nv_quantize(w5d, None, wnq, wns, wng)
+        mxq.quantize(w5d, wmq, wms)
         ops.append(("nv_gemm_w4a16_4096x8192x4096", lambda: mxq.nv_gemm(wnq, wns, wng, x5d, y=y5n),
-                    nv_bytes(n5, k5) + m5 * k5 * 2 + m5 * n5 * 2, 2 * m5 * n5 * k5))
+                    nv_bytes(n5, k5) + m5 * k5 * 2 + m5 * n5 * 2, 2 * m5 * n5 * k5, "bf16"))
         ops.append(("mx_gemm_w4a16_4096x8192x4096", lambda: mxq.gemv_w4a16(wmq, wms, x5d, y=y5m),
-                    mx_bytes(n5, k5) + m5 * k5 * 2 + m5 * n5 * 2, 2 * m5 * n5 * k5))
+                    mx_bytes(n5, k5) + m5 * k5 * 2 + m5 * n5 * 2, 2 * m5 * n5 * k5, "bf16"))
+        keep["c5"] = (w5, x5, w5d, x5d, y5m, y5n)
     if "copy" in parts:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
         # counters calibrate the HBM byte counts of the other kernels
         csrc = torch.empty(1 << 30, dtype=u8, device=dev)
         cdst = torch.empty_like(csrc)
         csrc.fill_(1)
-        ops.append(("copy_1GiB", lambda: cdst.copy_(csrc), 2 << 30, 0))
+        ops.append(("copy_1GiB", lambda: cdst.copy_(csrc), 2 << 30, 0, "hbm"))
+    if args.ops:
+        pref = tuple(args.ops.split(","))
+        ops = [o for o in ops if o[0].startswith(pref)]
     torch.cuda.synchronize()
     print(f"inputs ready in {time.time() - t_gen:.1f}s; warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    nops = len(ops)
 
-    def run_step(evs):
-        for i, (_, fn, _, _) in enumerate(ops):
-            if evs is not None:
-                evs[i][0].record(stream)
+    def run_step():
+        for _, fn, _, _, _ in ops:
             fn()
-            if evs is not None:
-                evs[i][1].record(stream)
 
     for _ in range(args.warmup):
-        run_step(None)
+        run_step()
     torch.cuda.synchronize()
-    # timed region 1: K steps, one pass of the hot path each; every call is
-    # also bracketed by its own pair of events (single-launch times)
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(nops)]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # 1. K steps of the whole path
     t0 = time.perf_counter()
-    for st in range(args.steps):
-        run_step(events[st])
+    for _ in range(args.steps):
+        run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # timed region 2: per op, BURST back-to-back launches between one pair of
-    # events; elapsed / BURST is the kernel's average launch duration (inter-
-    # launch gaps included), free of the few microseconds that an event pair
-    # adds around a single short launch.  This is the figure the rooflines use.
-    burst = {}
-    for i, (name, fn, _, _) in enumerate(ops):
+    print(f"{args.steps} steps: {wall / args.steps * 1e3:.3f} ms per step", file=sys.stderr, flush=True)
+
+    # 2 and 3: per op, single launches and bursts
+    per_op = {}
+    for name, fn, nbytes, flops, bound in ops:
+        fn()
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.singles)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        single = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
         reps = []
-        for _ in range(max(1, args.steps // 4)):
+        for _ in range(args.bursts):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(BURST):
@@ -325,52 +352,50 @@ def main():
             e1.record(stream)
             e1.synchronize()
             reps.append(e0.elapsed_time(e1) / BURST)
-        burst[name] = float(np.median(reps))
-    per_op = {}
-    for i, (name, _, nbytes, flops) in enumerate(ops):
-        ms = [events[st][i][0].elapsed_time(events[st][i][1]) for st in range(args.steps)]
-        avg = burst[name]
+        ms = float(np.median(reps))
         per_op[name] = {
-            "ms": round(avg, 5),
-            "ms_single_median": round(float(np.median(ms)), 5),
-            "ms_single_min": round(float(np.min(ms)), 5),
-            "GB/s": round(nbytes / avg / 1e6, 1),
-            "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None,
+            "ms": round(ms, 5),
+            "ms_single_median": round(float(np.median(single)), 5),
+            "ms_single_min": round(float(single.min()), 5),
+            "singles": len(single),
+            "GB/s": round(nbytes / ms / 1e6, 1),
+            "TFLOP/s": round(flops / ms / 1e9, 1) if flops else None,
             "bytes": nbytes,
             "flops": flops,
+            "bound": bound,
         }
-        print(f"  {name:34s} {avg * 1e3:10.2f} us (single {np.median(ms) * 1e3:8.2f})  {nbytes / avg / 1e6:9.1f} GB/s"
-              + (f"  {flops / avg / 1e9:9.1f} TFLOP/s" if flops else ""), file=sys.stderr, flush=True)
+        print(f"  {name:36s} {ms * 1e3:9.2f} us (single median {np.median(single) * 1e3:8.2f}, "
+              f"min {single.min() * 1e3:8.2f})  {nbytes / ms / 1e6:9.1f} GB/s"
+              + (f"  {flops / ms / 1e9:9.1f} TFLOP/s" if flops else ""), file=sys.stderr, flush=True)
 
-    def roof(name, bound):
+    ceil = None if args.no_ceilings else measure_ceilings(torch, dev, stream)
+
+    def roof(name):
         r = per_op[name]
-        if bound == "hbm":
-            a, p, u = r["GB/s"], HBM_PEAK_GBS, "GB/s"
-        elif bound == "mfma_fp4":
-            a, p, u = r["TFLOP/s"], FP4_PEAK_TFLOPS, "TFLOP/s"
-        elif bound == "mfma_fp8":
-            a, p, u = r["TFLOP/s"], FP8_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            a, p, u = r["TFLOP/s"], BF16_PEAK_TFLOPS, "TFLOP/s"
-        out = {"bound": "hbm" if bound == "hbm" else "mfma", "achieved": a, "peak": p, "unit": u,
-               "frac": round(a / p, 4), "traffic": traffic_for(name)}
+        bound = r["bound"]
+        a = r["GB/s"] if bound == "hbm" else r["TFLOP/s"]
+        p = PEAKS[bound]
+        out = {"bound": "hbm" if bound == "hbm" else "mfma", "achieved": a, "peak": p,
+               "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": round(a / p, 4),
+               "traffic": traffic_for(name)}
+        if bound != "hbm":
+            out["dtype"] = {"fp4": "e2m1 x e2m1", "fp8": "e4m3 x e2m1", "bf16": "bf16 x bf16"}[bound]
+        # single-launch figure beside the steady-state one
+        out["achieved_single_median"] = round((r["bytes"] if bound == "hbm" else r["flops"])
+                                              / r["ms_single_median"] / (1e6 if bound == "hbm" else 1e9), 1)
+        if ceil:
+            c = ceil.get({"hbm": "hbm_read_GBps", "fp4": "mfma_fp4_TFLOPs", "fp8": "mfma_fp8_TFLOPs",
+                          "bf16": "mfma_bf16_TFLOPs"}[bound])
+            if c:
+                out["ceiling"] = c
+                out["frac_of_ceiling"] = round(a / c, 4)
         return out
 
-    rooflines = {}
-    for name in per_op:
-        if name.startswith("gemm_w4a4"):  # both output kinds
-            rooflines[name] = roof(name, "mfma_fp4")
-        elif name.startswith("gemm_w4a8"):
-            rooflines[name] = roof(name, "mfma_fp8")
-        elif "gemm_w4a16_4096" in name:
-            rooflines[name] = roof(name, "mfma_bf16")
-        else:
-            rooflines[name] = roof(name, "hbm")
+    rooflines = {name: roof(name) for name in per_op}
 
-    head = "gemv_w4a16_m1"
     result = {
         "metric": METRIC,
-        "value": per_op[head]["GB/s"] if head in per_op else None,
+        "value": per_op[HEAD]["GB/s"] if HEAD in per_op else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -386,19 +411,155 @@ def main():
                         "W4A4 GEMM 8192^3; dynamic quantize 16384x8192 bf16; NVFP4 vs MXFP4 W 8192x4096, X 4096x4096",
             "gemv_n": 28672, "gemv_k": 8192, "gemv_m": 1,
         },
-        "roofline": rooflines.get(head),
+        "roofline": rooflines.get(HEAD),
         "secondary": None,
+        "ceilings": ceil,
         "rooflines": rooflines,
         "kernels": per_op,
     }
     if "gemm_w4a4_8192" in per_op:
-        r = per_op["gemm_w4a4_8192"]
+        r = rooflines["gemm_w4a4_8192"]
         result["secondary"] = {"metric": "W4A4 GEMM TFLOPS (8192^3, MXFP4 x MXFP4, bf16 out)",
-                               "value": r["TFLOP/s"], "unit": "TFLOP/s",
-                               "frac_of_mxfp4_peak": round(r["TFLOP/s"] / FP4_PEAK_TFLOPS, 4)}
+                               "value": r["achieved"], "unit": "TFLOP/s", "frac_of_mxfp4_peak": r["frac"],
+                               "frac_of_measured_mfma_ceiling": r.get("frac_of_ceiling")}
+    if not args.no_metrics:
+        result["metrics"] = quality_metrics(torch, mxq, keep)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
+
+
+# ---------------------------------------------------------------- on-box ceilings
+
+def measure_ceilings(torch, dev, stream):
+    """Ceilings measured on this machine by libmxq_ceiling.so's kernels:
+    - hbm_read_GBps: the best of a small sweep (loads in flight x grid) of a
+      pure streaming read of 124,854,272 bytes (the m = 1 decode GEMV's
+      algorithmic bytes) per launch, rotating over copies that defeat the
+      256 MB cache, burst-timed like the library's ops; hbm_read_1GiB_GBps
+      the same for 1 GiB per launch;
+    - mfma_fp4_TFLOPs / mfma_bf16_TFLOPs: back-to-back 32x32 MFMAs on random
+      register operands on every SIMD (8 waves per CU), with the shader clock
+      read in the kernel (core-cycle counter over the constant-rate counter);
+      the E4M3 x E2M1 issue ceiling is half the E2M1 one (the instruction
+      takes twice the cycles).
+    """
+    path = os.path.join(ROOT, "mxfp4_microscaling_quantization_mxq_amd", "libmxq_ceiling.so")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mxqc_stream_read.argtypes = [P, I64, I, I, P, P]
+    lib.mxqc_mfma_fp4.argtypes = [P, I64, I, P, P, P]
+    lib.mxqc_mfma_bf16.argtypes = [P, I64, I, P, P, P]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+
+    def timed(fn, reps=5, burst=BURST):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(burst):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1) / burst)
+        return float(np.median(t))
+
+    sink = torch.empty(65536, dtype=torch.float32, device=dev)
+    for label, nbytes in (("hbm_read_GBps", 124_854_272), ("hbm_read_1GiB_GBps", 1 << 30)):
+        ncp = max(2, -(-COLD_BYTES // nbytes))
+        buf = torch.empty(ncp * nbytes, dtype=torch.uint8, device=dev)
+        buf.fill_(0x5A)
+        best = None
+        for unroll in (4, 8, 16):
+            for blocks in (1024, 2048, 4096, 8192):
+                st = {"i": 0}
+
+                def fn(unroll=unroll, blocks=blocks):
+                    off = (st["i"] % ncp) * nbytes
+                    st["i"] += 1
+                    rc = lib.mxqc_stream_read(ctypes.c_void_p(buf.data_ptr() + off), nbytes, unroll, blocks,
+                                              ctypes.c_void_p(sink.data_ptr()), sptr)
+                    assert rc == 0, rc
+                ms = timed(fn)
+                gbs = nbytes / ms / 1e6
+                if best is None or gbs > best[0]:
+                    best = (gbs, unroll, blocks, ms)
+        out[label] = round(best[0], 1)
+        out[label.replace("_GBps", "_shape")] = {"loads_in_flight": best[1], "blocks": best[2],
+                                                 "us": round(best[3] * 1e3, 2)}
+        del buf
+    src = torch.randint(0, 256, (8192,), dtype=torch.uint8, device=dev)
+    wall_khz = lib.mxqc_wall_clock_khz()
+    out["peak_sclk_MHz"] = lib.mxqc_peak_clock_khz() / 1e3
+    for label, fnname, per_mfma in (("mfma_fp4_TFLOPs", "mxqc_mfma_fp4", 2 * 32 * 32 * 64),
+                                    ("mfma_bf16_TFLOPs", "mxqc_mfma_bf16", 2 * 32 * 32 * 16)):
+        blocks, iters = 1024, 2048
+        clk = torch.zeros(blocks * 8 * 4, dtype=torch.int64, device=dev)
+        f = getattr(lib, fnname)
+
+        def fn():
+            rc = f(ctypes.c_void_p(src.data_ptr()), iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                   ctypes.c_void_p(clk.data_ptr()), sptr)
+            assert rc == 0, rc
+        ms = timed(fn, reps=3, burst=4)
+        flops = blocks * 8 * 8 * iters * per_mfma
+        out[label] = round(flops / ms / 1e9, 1)
+        c = clk.view(-1, 4).cpu().numpy().astype(np.float64)
+        mhz = (c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * wall_khz / 1e3
+        out[label.replace("_TFLOPs", "_sclk_MHz")] = round(float(np.median(mhz)), 1)
+    out["mfma_fp8_TFLOPs"] = round(out["mfma_fp4_TFLOPs"] / 2, 1)
+    print(f"  ceilings: {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
+
+
+# ---------------------------------------------------------------- quality (host, untimed)
+
+def quality_metrics(torch, mxq, keep):
+    """NMSE and cosine (float64, host) of the GPU's quantized tensors and
+    products: the tiny reference's W and y, and for NVFP4 and MXFP4 the
+    8192x4096 W, the 4096x4096 X and the product Y = X W^T, Y against the
+    product of the unquantized inputs (W4A16: only W is quantized in Y)."""
+    from mxfp4_microscaling_quantization_mxq_amd.metrics import bf16_bits_to_f64, nmse_cosine
+    from mxfp4_microscaling_quantization_mxq_amd import synth
+
+    def host_bits(t):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def rnd(p):
+        return [round(p[0], 6), round(p[1], 6)]
+
+    out = {}
+    if "tiny" in keep:
+        w1, x1, y1, g1 = keep["tiny"]
+        xf = synth.bf16_bits_to_f32(x1).astype(np.float64)
+        yexact = xf @ w1.astype(np.float64).T
+        out["tiny_256x512"] = {"MXFP4": {"W": rnd(nmse_cosine(w1, y1.cpu().numpy())),
+                                         "Y": rnd(nmse_cosine(yexact, bf16_bits_to_f64(host_bits(g1))))}}
+    if "c5" in keep:
+        w5, x5, w5d, x5d, y5m, y5n = keep["c5"]
+        wf = synth.bf16_bits_to_f32(w5).astype(np.float64)
+        xf = synth.bf16_bits_to_f32(x5).astype(np.float64)
+        yexact = xf @ wf.T
+        c5 = {}
+        for fmt in ("MXFP4", "NVFP4"):
+            rows = {}
+            for tname, tsrc, tref in (("W", w5d, wf), ("X", x5d, xf)):
+                if fmt == "MXFP4":
+                    q, s = mxq.quantize(tsrc)
+                    deq = mxq.dequantize(q, s, torch.float32)
+                else:
+                    q, s, g = mxq.nv_quantize(tsrc)
+                    deq = mxq.nv_dequantize(q, s, g, torch.float32)
+                rows[tname] = rnd(nmse_cosine(tref, deq.cpu().numpy()))
+            y = y5m if fmt == "MXFP4" else y5n
+            rows["Y"] = rnd(nmse_cosine(yexact, bf16_bits_to_f64(host_bits(y))))
+            c5[fmt] = rows
+        out["nv_vs_mx_8192x4096x4096"] = c5
+    print(f"  metrics: {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
 
 
 # ---------------------------------------------------------------- traffic from counters
@@ -441,8 +602,9 @@ def traffic_for(name):
 
 def cpu_baseline():
     """The oracle (plain C, OpenMP) on a bounded sample of the same workloads:
-    the full decode GEMV (m = 1) repeated for about 8 s, a 1024 x 1024 output
-    block of the W4A4 GEMM, and the full dynamic quantize."""
+    the full decode GEMV (m = 1) repeated for about 8 s, the 1024 x 1024
+    top-left output block of the 8192^3 W4A4 GEMM (rows 0..1023 of the
+    workload's own A and B, k = 8192), and the full dynamic quantize."""
     import oracle
     from mxfp4_microscaling_quantization_mxq_amd import synth
 
@@ -461,7 +623,8 @@ def cpu_baseline():
         reps += 1
         del wd
     gemv_gbs = reps * gemv_bytes(n2, k2, 1) / t_gemv / 1e9
-    a, b = synth.w4a4_operands(m=1024, n=1024)
+    a, b = synth.w4a4_operands()
+    a, b = np.ascontiguousarray(a[:1024]), np.ascontiguousarray(b[:1024])
     qa, sa = oracle.mx_quantize(a)
     qb, sb = oracle.mx_quantize(b)
     t0 = time.perf_counter()
@@ -477,7 +640,8 @@ def cpu_baseline():
         "sample": f"decode W4A16 GEMV m=1 on the full 28672x8192 weight, {reps} runs in {t_gemv:.1f}s "
                   f"(dequantize to double + double dot products); bytes counted as for the GPU kernel",
         "gemm_w4a4_tflops": round(gemm_tflops, 5),
-        "gemm_sample": f"1024x1024 outputs of the 8192^3 W4A4 GEMM (k = 8192), {t_gemm:.2f}s",
+        "gemm_sample": f"C[0:1024, 0:1024] of the 8192^3 W4A4 GEMM: rows 0..1023 of the workload's own A and B "
+                       f"(k = 8192), dequantize + double products, {t_gemm:.2f}s",
         "quantize_GBps": round(quant_bytes(16384, 8192) / t_q / 1e9, 3),
         "quantize_sample": f"full 16384x8192 bf16 dynamic quantize, {t_q:.2f}s",
         "cpu": _cpu_model(),

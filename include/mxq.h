@@ -44,18 +44,16 @@
  *     not alias inputs.  Work is enqueued on `stream` (0 = default stream)
  *     and the call returns without waiting for it.
  *   - Validation happens before anything is launched; on any error nothing
- *     is written.  A negative size -> MXQ_ERROR_INVALID_VALUE.  k not a
- *     multiple of the block size -> MXQ_ERROR_INVALID_VALUE.  A NULL pointer
- *     for a non-empty operand -> MXQ_ERROR_INVALID_VALUE.  A base pointer
+ *     is written.  Any size (rows, k, m or n) below 1 ->
+ *     MXQ_ERROR_INVALID_VALUE: an empty problem is rejected, not a no-op.
+ *     k not a multiple of the block size -> MXQ_ERROR_INVALID_VALUE.  A NULL
+ *     pointer -> MXQ_ERROR_INVALID_VALUE.  A base pointer
  *     that is not 16-byte aligned (4-byte for the scalar NVFP4 tensor scale)
  *     -> MXQ_ERROR_MISALIGNED.  No HIP device, or a device that is not
  *     gfx950 -> MXQ_ERROR_NOT_SUPPORTED.  A failed launch ->
  *     MXQ_ERROR_LAUNCH_FAILURE.  Faults inside a kernel are asynchronous and
  *     surface at the caller's next synchronization.
- *   - Empty problems are no-ops that return MXQ_SUCCESS (NULL pointers are
- *     then allowed), except that a product with k == 0 and a non-empty
- *     output writes zeros.
- *   - Non-finite inputs (NaN, Inf) are outside the contract.  Products whose
+ * *   - Non-finite inputs (NaN, Inf) are outside the contract.  Products whose
  *     exact value, or whose dequantized operands, leave the fp32 range
  *     (scale codes above 250 or below about 16) are outside the contract.
  *   - Results are deterministic: the same call gives bitwise identical
@@ -153,7 +151,8 @@ MXQ_API mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *s, int64_t ro
  * [infra-guide sec. 4.2 and 5].  Any m >= 1.  Memory-bound decode kernels
  * up to m = 127; for n >= 14336 and k % 512 == 0 a weight-streaming ring of
  * up to 64 activation rows, with m = 65..128 as two launches of it.  Larger
- * m takes a bf16-MFMA GEMM tile.  k % 32 == 0.
+ * m takes a bf16-MFMA GEMM tile (for k < 2^23; longer rows stay on the
+ * decode kernels).  k % 32 == 0.
  */
 MXQ_API mxq_status mxq_gemv_w4a16(const uint8_t *wq, const uint8_t *ws, int64_t n,
                           int64_t k, const void *x, int64_t m, void *y,
@@ -198,7 +197,7 @@ MXQ_API mxq_status mxq_gemm_w4a8(const uint8_t *aq8, const uint8_t *as,
  * kernel's epilogue, so the 16-bit product never reaches memory.  The codes
  * cq[m][n/2] and E8M0 scales cs[m][n/32] are bit-identical to mxq_quantize
  * of the bf16 product (the same quantizer runs on the same bf16 values).
- * n % 32 == 0, k % 32 == 0; k == 0 writes the codes of a zero product.
+ * n % 32 == 0, k % 32 == 0.
  * [TransFP4 page sec. 2.5: no 16-bit copy is materialized; "FP4
  * quantization analysis" page, QuTLASS kernel section: custom epilogues
  * fuse the quantization of the output.]
@@ -222,8 +221,8 @@ MXQ_API mxq_status mxq_gemm_w4a4_quant(const uint8_t *aq, const uint8_t *as,
  * weight rows quantizes the bf16 activation tile again, which pays while the
  * weight stream dominates.  1 <= m <= 16, k % 512 == 0, k <= 2^24, else
  * MXQ_ERROR_INVALID_VALUE (larger batches: mxq_quantize once, then
- * mxq_gemm_w4a4, which is faster there).  m == 0 or n == 0: no-op; k == 0
- * writes zeros.  Errors otherwise as mxq_gemm_w4a4.
+ * mxq_gemm_w4a4, which is faster there).  Errors otherwise as
+ * mxq_gemm_w4a4.
  */
 MXQ_API mxq_status mxq_gemm_w4a4_dynamic(const void *x, const uint8_t *bq,
                                  const uint8_t *bs, int64_t m, int64_t n,
@@ -240,9 +239,8 @@ MXQ_API mxq_status mxq_gemm_w4a4_dynamic(const void *x, const uint8_t *bq,
  * load stage.]  x bf16 [m][k]; B = (bq[n][k/2], bs[n][k/32]); c written as
  * cdt.  For decode-sized batches, as mxq_gemm_w4a4_dynamic: 1 <= m <= 16,
  * k % 512 == 0, k <= 2^24, else MXQ_ERROR_INVALID_VALUE (larger batches:
- * mxq_quantize_fp8 once, then mxq_gemm_w4a8, which is faster there).  m ==
- * 0 or n == 0: no-op; k == 0 writes zeros.  Errors otherwise as
- * mxq_gemm_w4a4.
+ * mxq_quantize_fp8 once, then mxq_gemm_w4a8, which is faster there).
+ * Errors otherwise as mxq_gemm_w4a4.
  */
 MXQ_API mxq_status mxq_gemm_w4a8_dynamic(const void *x, const uint8_t *bq,
                                  const uint8_t *bs, int64_t m, int64_t n,

@@ -1,0 +1,178 @@
+// ceilings.hip -- measurement kernels, not part of the method: the on-box
+// ceilings against which the library's kernels are judged (libmxq_ceiling.so,
+// loaded by the benchmark only).
+//
+//   mxqc_stream_read   pure streaming read of a byte range (the HBM ceiling a
+//                      weight-streaming kernel of the same size can reach)
+//   mxqc_mfma_fp4      back-to-back V_MFMA_SCALE_F32_32X32X64_F8F6F4 with two
+//                      E2M1 operands on registers (the fp4 MFMA issue ceiling)
+//   mxqc_mfma_bf16     back-to-back V_MFMA_F32_32X32X16_BF16 (the bf16 one)
+//
+// The MFMA kernels also read the core-cycle and constant-rate counters at
+// the start and end of every wave, so the caller can derive the shader clock
+// the matrix units actually ran at.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+// Each lane keeps U 16-byte loads in flight; a block of 256 lanes reads
+// 256 * 16 * U contiguous bytes per step, blocks stride over the range.
+template <int U>
+__global__ __launch_bounds__(256) void k_stream_read(const i32x4* __restrict__ p, int64_t n16, float* __restrict__ sink) {
+  const int64_t step = (int64_t)gridDim.x * 256 * U;
+  int acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += step) {
+    i32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : (i32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // the xor is kept alive by a store no input makes true in practice
+  if (acc == 0x7F3A5C11) sink[blockIdx.x] = (float)acc;
+}
+
+struct Clocks {
+  unsigned long long c0, c1, w0, w1;
+};
+
+__device__ __forceinline__ void record(Clocks* clk, unsigned long long c0, unsigned long long w0) {
+  const unsigned long long c1 = __builtin_readcyclecounter();
+  const unsigned long long w1 = wall_clock64();
+  if ((threadIdx.x & 63) == 0) {
+    Clocks* d = clk + blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+    d->c0 = c0;
+    d->c1 = c1;
+    d->w0 = w0;
+    d->w1 = w1;
+  }
+}
+
+// 8 independent 32x32 accumulators per wave.  Operands are 4 A and 4 B
+// fragments of random bytes (the matrix units' power, and so the clock they
+// sustain, depends on how many operand bits toggle), paired round-robin so
+// consecutive instructions see different data.
+__global__ __launch_bounds__(512) void k_mfma_fp4(const i32x4* __restrict__ src, int64_t iters,
+                                                  float* __restrict__ sink, Clocks* __restrict__ clk) {
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  const unsigned long long w0 = wall_clock64();
+  const int lane = threadIdx.x & 63;
+  i32x8 a[4], b[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const i32x4 va = src[j * 64 + lane], vb = src[(4 + j) * 64 + lane];
+    a[j] = (i32x8){va.x, va.y, va.z, va.w, 0, 0, 0, 0};
+    b[j] = (i32x8){vb.x, vb.y, vb.z, vb.w, 0, 0, 0, 0};
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = (f32x16){};
+  for (int64_t it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[(j + u) & 3], acc[j], 4, 4, 0, 127,
+                                                                   0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) s += acc[j][0] + acc[j][15];
+  if (s == 1.2345678e-30f) sink[blockIdx.x] = s;
+  record(clk, c0, w0);
+}
+
+__global__ __launch_bounds__(512) void k_mfma_bf16(const i32x4* __restrict__ src, int64_t iters,
+                                                   float* __restrict__ sink, Clocks* __restrict__ clk) {
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  const unsigned long long w0 = wall_clock64();
+  const int lane = threadIdx.x & 63;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    // random bf16 with the exponent field kept near 1 (finite products)
+    i32x4 va = src[j * 64 + lane], vb = src[(4 + j) * 64 + lane];
+    va = (va & 0x807F807F) | 0x3F003F00;
+    vb = (vb & 0x807F807F) | 0x3F003F00;
+    a[j] = __builtin_bit_cast(bf16x8, va);
+    b[j] = __builtin_bit_cast(bf16x8, vb);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = (f32x16){};
+  for (int64_t it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j + u) & 3], acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) s += acc[j][0] + acc[j][15];
+  if (s == 1.2345678e-30f) sink[blockIdx.x] = s;
+  record(clk, c0, w0);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads bytes (a multiple of 16, 16-byte aligned) of device memory at p with
+// `unroll` (4, 8 or 16) loads in flight per lane on `blocks` blocks of 256
+// lanes.  sink: blocks floats (never written in practice).  Returns a
+// hipError_t code.
+__attribute__((visibility("default"))) int mxqc_stream_read(const void* p, int64_t bytes, int unroll, int blocks,
+                                                            float* sink, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (unroll == 4)
+    hipLaunchKernelGGL(k_stream_read<4>, dim3(blocks), dim3(256), 0, st, (const i32x4*)p, n16, sink);
+  else if (unroll == 16)
+    hipLaunchKernelGGL(k_stream_read<16>, dim3(blocks), dim3(256), 0, st, (const i32x4*)p, n16, sink);
+  else
+    hipLaunchKernelGGL(k_stream_read<8>, dim3(blocks), dim3(256), 0, st, (const i32x4*)p, n16, sink);
+  return (int)hipGetLastError();
+}
+
+// `blocks` blocks of 8 waves, each wave 8 * iters MFMAs (iters a multiple
+// of 4).  src: 512 x 16 bytes of random operand data (device); clk: 4
+// uint64 per wave (core cycles at start and end, constant-rate counter at
+// start and end); sink: blocks floats (never written in practice).
+__attribute__((visibility("default"))) int mxqc_mfma_fp4(const void* src, int64_t iters, int blocks, float* sink,
+                                                         void* clk, hipStream_t st) {
+  hipLaunchKernelGGL(k_mfma_fp4, dim3(blocks), dim3(512), 0, st, (const i32x4*)src, iters, sink, (Clocks*)clk);
+  return (int)hipGetLastError();
+}
+
+__attribute__((visibility("default"))) int mxqc_mfma_bf16(const void* src, int64_t iters, int blocks, float* sink,
+                                                          void* clk, hipStream_t st) {
+  hipLaunchKernelGGL(k_mfma_bf16, dim3(blocks), dim3(512), 0, st, (const i32x4*)src, iters, sink, (Clocks*)clk);
+  return (int)hipGetLastError();
+}
+
+// Rate of the constant counter the MFMA kernels read (kHz), and the
+// device's peak shader clock (kHz), for the current device; -1 on error.
+__attribute__((visibility("default"))) int mxqc_wall_clock_khz(void) {
+  int dev = 0, v = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return -1;
+  return v;
+}
+
+__attribute__((visibility("default"))) int mxqc_peak_clock_khz(void) {
+  int dev = 0, v = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate, dev) != hipSuccess)
+    return -1;
+  return v;
+}
+
+}  // extern "C"

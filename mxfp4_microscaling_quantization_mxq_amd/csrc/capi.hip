@@ -58,7 +58,7 @@ extern "C" {
 const char* mxq_status_string(mxq_status s) {
   switch (s) {
     case MXQ_SUCCESS: return "success";
-    case MXQ_ERROR_INVALID_VALUE: return "invalid value (null pointer, negative size, or k not a multiple of the block size)";
+    case MXQ_ERROR_INVALID_VALUE: return "invalid value (null pointer, a size below 1, or k not a multiple of the block size)";
     case MXQ_ERROR_MISALIGNED: return "misaligned pointer (16-byte alignment required)";
     case MXQ_ERROR_NOT_SUPPORTED: return "not supported (no HIP device, or the device is not gfx950)";
     case MXQ_ERROR_LAUNCH_FAILURE: return "kernel launch failed";
@@ -66,12 +66,14 @@ const char* mxq_status_string(mxq_status s) {
   return "unknown status";
 }
 
-int mxq_version(void) { return 100; }
+int mxq_version(void) { return 200; }
+
+// Every size must be at least 1: an empty problem is an invalid argument,
+// not a no-op, so a caller's shape bug surfaces at the call.
 
 mxq_status mxq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
                         hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!x || !q || !s) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
@@ -83,8 +85,7 @@ mxq_status mxq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, u
 mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, int hk, uint8_t* q,
                                  uint8_t* s, hipStream_t stream) {
   if (hk != 16 && hk != 32 && hk != 64 && hk != 128) return MXQ_ERROR_INVALID_VALUE;
-  if (rows < 0 || k < 0 || k % 32 != 0 || k % hk != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || k % hk != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!x || !q || !s) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
@@ -95,8 +96,7 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype xdt, int64_t rows, int
 
 mxq_status mxq_quantize_fp8(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, uint8_t* q, uint8_t* s,
                             hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!x || !q || !s) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
@@ -107,8 +107,7 @@ mxq_status mxq_quantize_fp8(const void* x, mxq_dtype xdt, int64_t rows, int64_t 
 
 mxq_status mxq_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t k, void* y, mxq_dtype ydt,
                           hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!q || !s || !y) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(s) || !aligned16(y)) return MXQ_ERROR_MISALIGNED;
@@ -120,18 +119,10 @@ mxq_status mxq_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int6
 static mxq_status w4a16_common(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gs, int64_t n,
                                int64_t k, const void* x, int64_t m, void* y, mxq_dtype ydt, hipStream_t stream) {
   const int64_t blk = nv ? 16 : 32;
-  if (n < 0 || k < 0 || m < 0 || k % blk != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
-  if (n == 0 || m == 0) return MXQ_SUCCESS;
+  if (n < 1 || k < 1 || m < 1 || k % blk != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
   if ((m + 15) / 16 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!y) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(y)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    return launched(mxq::launch_zero(y, m * n, ydt == MXQ_BF16, stream));
-  }
-  if (!wq || !ws || !x || (nv && !gs)) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(wq) || !aligned16(ws) || !aligned16(x)) return MXQ_ERROR_MISALIGNED;
+  if (!wq || !ws || !x || !y || (nv && !gs)) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(wq) || !aligned16(ws) || !aligned16(x) || !aligned16(y)) return MXQ_ERROR_MISALIGNED;
   if (nv && ((uintptr_t)gs & 3u)) return MXQ_ERROR_MISALIGNED;
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
@@ -148,108 +139,75 @@ mxq_status nvq_gemm(const uint8_t* wq, const uint8_t* ws, const float* wgscale, 
   return w4a16_common(true, wq, ws, wgscale, n, k, x, m, y, ydt, stream);
 }
 
+// Shared checks of the block-scaled products (A codes of either format).
+static mxq_status product_args(const void* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                               int64_t n, int64_t k, const void* c) {
+  if (m < 1 || n < 1 || k < 1 || k % 32 != 0) return MXQ_ERROR_INVALID_VALUE;
+  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (!aq || !as || !bq || !bs || !c) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs) || !aligned16(c))
+    return MXQ_ERROR_MISALIGNED;
+  return MXQ_SUCCESS;
+}
+
 mxq_status mxq_gemm_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                          int64_t n, int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!c) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
-  }
-  if (!aq || !as || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
-  mxq_status d = check_device();
-  if (d != MXQ_SUCCESS) return d;
+  if (!valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
+  mxq_status e = product_args(aq, as, bq, bs, m, n, k, c);
+  if (e == MXQ_SUCCESS) e = check_device();
+  if (e != MXQ_SUCCESS) return e;
   return launched(mxq::launch_w4a4(aq, as, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
 }
 
 mxq_status mxq_gemm_w4a8(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                          int64_t n, int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!c) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
-  }
-  if (!aq8 || !as || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(aq8) || !aligned16(as) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
-  mxq_status d = check_device();
-  if (d != MXQ_SUCCESS) return d;
+  if (!valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
+  mxq_status e = product_args(aq8, as, bq, bs, m, n, k, c);
+  if (e == MXQ_SUCCESS) e = check_device();
+  if (e != MXQ_SUCCESS) return e;
   return launched(mxq::launch_w4a8(aq8, as, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
+}
+
+mxq_status mxq_gemm_w4a4_quant(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
+                               int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t stream) {
+  mxq_status e = product_args(aq, as, bq, bs, m, n, k, cq);
+  if (e != MXQ_SUCCESS) return e;
+  if (n % 32 != 0 || !cs) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(cs)) return MXQ_ERROR_MISALIGNED;
+  e = check_device();
+  if (e != MXQ_SUCCESS) return e;
+  return launched(mxq::launch_w4a4_mx(aq, as, bq, bs, m, n, k, cq, cs, stream));
+}
+
+// The in-GEMM activation quantize serves decode-sized batches only.
+static mxq_status dynamic_args(const void* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n, int64_t k,
+                               const void* c, mxq_dtype cdt) {
+  if (m < 1 || n < 1 || k < 1 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
+  if (m > 16 || k % 512 != 0 || k > (1 << 24) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
+  if (!x || !bq || !bs || !c) return MXQ_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(bq) || !aligned16(bs) || !aligned16(c)) return MXQ_ERROR_MISALIGNED;
+  return MXQ_SUCCESS;
 }
 
 mxq_status mxq_gemm_w4a4_dynamic(const void* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                  int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if (m > 16 || k % 512 != 0 || k > (1 << 24) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!c) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
-  }
-  if (!x || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(x) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
-  mxq_status d = check_device();
-  if (d != MXQ_SUCCESS) return d;
+  mxq_status e = dynamic_args(x, bq, bs, m, n, k, c, cdt);
+  if (e == MXQ_SUCCESS) e = check_device();
+  if (e != MXQ_SUCCESS) return e;
   return launched(mxq::launch_w4a4_dynamic((const uint16_t*)x, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
 }
 
 mxq_status mxq_gemm_w4a8_dynamic(const void* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                  int64_t k, void* c, mxq_dtype cdt, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || !valid_dtype(cdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if (m > 16 || k % 512 != 0 || k > (1 << 24) || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!c) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(c)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    return launched(mxq::launch_zero(c, m * n, cdt == MXQ_BF16, stream));
-  }
-  if (!x || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(x) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
-  mxq_status d = check_device();
-  if (d != MXQ_SUCCESS) return d;
+  mxq_status e = dynamic_args(x, bq, bs, m, n, k, c, cdt);
+  if (e == MXQ_SUCCESS) e = check_device();
+  if (e != MXQ_SUCCESS) return e;
   return launched(mxq::launch_w4a8_dynamic((const uint16_t*)x, bq, bs, m, n, k, c, cdt == MXQ_BF16, stream));
-}
-
-mxq_status mxq_gemm_w4a4_quant(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
-                               int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || n % 32 != 0) return MXQ_ERROR_INVALID_VALUE;
-  if (m == 0 || n == 0) return MXQ_SUCCESS;
-  if ((m + 127) / 128 > kMaxGridY || n > kMaxElems / 16) return MXQ_ERROR_INVALID_VALUE;
-  if (!cq || !cs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(cq) || !aligned16(cs)) return MXQ_ERROR_MISALIGNED;
-  if (k == 0) {
-    // the product is zero: the codes and scales of quantizing zeros
-    mxq_status d = check_device();
-    if (d != MXQ_SUCCESS) return d;
-    mxq_status e = launched(mxq::launch_zero_bytes(cq, m * n / 2, stream));
-    if (e != MXQ_SUCCESS) return e;
-    return launched(mxq::launch_zero_bytes(cs, m * n / 32, stream));
-  }
-  if (!aq || !as || !bq || !bs) return MXQ_ERROR_INVALID_VALUE;
-  if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs)) return MXQ_ERROR_MISALIGNED;
-  mxq_status d = check_device();
-  if (d != MXQ_SUCCESS) return d;
-  return launched(mxq::launch_w4a4_mx(aq, as, bq, bs, m, n, k, cq, cs, stream));
 }
 
 mxq_status nvq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, float* gscale, int compute_gscale,
                         uint8_t* q, uint8_t* s, hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 16 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 16 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!x || !q || !s || !gscale) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return MXQ_ERROR_MISALIGNED;
@@ -261,8 +219,7 @@ mxq_status nvq_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, f
 
 mxq_status nvq_dequantize(const uint8_t* q, const uint8_t* s, const float* gscale, int64_t rows, int64_t k, void* y,
                           mxq_dtype ydt, hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 16 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 16 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!q || !s || !gscale || !y) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(s) || !aligned16(y)) return MXQ_ERROR_MISALIGNED;
@@ -275,8 +232,7 @@ mxq_status nvq_dequantize(const uint8_t* q, const uint8_t* s, const float* gscal
 mxq_status mxq_transfp4_quantize(const void* x, mxq_dtype xdt, int64_t rows, int64_t k, float* gscale,
                                  int compute_gscale, uint8_t* q, uint8_t* s, uint8_t* meta, uint16_t* res,
                                  hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || !valid_dtype(xdt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!x || !q || !s || !meta || !res || !gscale) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(s) || !aligned16(meta) || !aligned16(res))
@@ -291,8 +247,7 @@ mxq_status mxq_transfp4_quantize(const void* x, mxq_dtype xdt, int64_t rows, int
 mxq_status mxq_transfp4_dequantize(const uint8_t* q, const uint8_t* s, const uint8_t* meta, const uint16_t* res,
                                    const float* gscale, int64_t rows, int64_t k, void* y, mxq_dtype ydt,
                                    hipStream_t stream) {
-  if (rows < 0 || k < 0 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
-  if (rows == 0 || k == 0) return MXQ_SUCCESS;
+  if (rows < 1 || k < 1 || k % 32 != 0 || !valid_dtype(ydt)) return MXQ_ERROR_INVALID_VALUE;
   if (rows > kMaxElems / k) return MXQ_ERROR_INVALID_VALUE;
   if (!q || !s || !meta || !res || !gscale || !y) return MXQ_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(s) || !aligned16(meta) || !aligned16(res) || !aligned16(y))

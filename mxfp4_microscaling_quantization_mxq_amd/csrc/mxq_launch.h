@@ -66,10 +66,4 @@ hipError_t launch_w4a8_dynamic(const uint16_t* x, const uint8_t* bq, const uint8
 hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                           int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t st);
 
-// Fills n bytes of y with zeros.
-hipError_t launch_zero_bytes(uint8_t* y, int64_t n, hipStream_t st);
-
-// Fills n elements of y (fp32 or bf16) with zeros.
-hipError_t launch_zero(void* y, int64_t n, bool bf16, hipStream_t st);
-
 }  // namespace mxq

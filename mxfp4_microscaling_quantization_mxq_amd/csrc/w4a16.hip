@@ -1100,7 +1100,10 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
       default: nv ? launch_decode_valu<true, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st)
                   : launch_decode_valu<false, 4>(wq, ws, gscale, n, k, x, y, bf16_out, st); break;
     }
-  } else if (m >= 128 && k % 64 == 0) {
+  } else if (m >= 128 && k % 64 == 0 && k < (1 << 23)) {
+    // the GEMM tile addresses its 256-row activation panel (512 k bytes)
+    // with 32-bit buffer offsets: k < 2^23 keeps it below 2^32 bytes;
+    // longer rows take the decode kernel (64-bit addressing)
     nv ? launch_gemm<true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
        : launch_gemm<false>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (nv) {

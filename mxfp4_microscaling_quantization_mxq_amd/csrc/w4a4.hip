@@ -505,32 +505,4 @@ hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* b
   return hipGetLastError();
 }
 
-// Zero fill used for products with an empty k.
-__global__ void k_zero(uint32_t* y, int64_t nwords) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nwords) y[i] = 0u;
-}
-__global__ void k_zero16(uint16_t* y, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) y[i] = 0u;
-}
-
-__global__ void k_zero_bytes(uint8_t* y, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) y[i] = 0u;
-}
-
-hipError_t launch_zero_bytes(uint8_t* y, int64_t n, hipStream_t st) {
-  hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero(void* y, int64_t n, bool bf16, hipStream_t st) {
-  if (bf16)
-    hipLaunchKernelGGL(k_zero16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (uint16_t*)y, n);
-  else
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (uint32_t*)y, n);
-  return hipGetLastError();
-}
-
 }  // namespace mxq
