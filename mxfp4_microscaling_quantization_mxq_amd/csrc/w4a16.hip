@@ -209,6 +209,15 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
   for (int mm = 0; mm < M; mm++)
     for (int r = 0; r < RB; r++) red[wave][mm][r][lane] = 0.f;
 
+  // MXFP4 with one k range per wave (6144 < k <= 8192, k % 256 == 0) and a
+  // whole block of rows: the scale bytes of the block's rows are one
+  // contiguous RB x ks stretch, read block-wide in full 128-byte lines
+  // (each wave's own 64-byte slices per row made half-line requests, which
+  // move half the bytes per request).  Block-uniform, so every wave meets
+  // the barrier below exactly once.
+  __shared__ __attribute__((aligned(16))) uint8_t sblk[kNv ? 16 : RB * 256];
+  const bool blk_sc = !kNv && U == 8 && RB % 8 == 0 && nkr == W && k % 256 == 0 && n0 + RB <= n;
+
   for (int64_t kr = wave; kr < nkr; kr += W) {
     const int64_t kb = kr * 2048 + 32 * lane;  // this lane's 32 k values
     const bool kval = kb < k;
@@ -235,7 +244,34 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
       // and every row's scale segment aligned to the per-lane load (8 B
       // MXFP4, 16 B NVFP4; NVFP4 rows are then 16-byte aligned too)
       const bool stage_sc = U == 8 && (kr + 1) * SB <= ks && ks % (SB / 8) == 0;
-      if (stage_sc) {
+      if (blk_sc) {
+        // the block's RB x ks scale bytes, contiguous, in full-line loads
+        // (one or two 8-byte pieces per thread) staged in LDS once, before
+        // the first rows' codes are consumed
+        u32x2 piece[RB / 8];
+        if (r0 == 0) {
+#pragma unroll
+          for (int p = 0; p < RB / 8; p++) {
+            const int64_t off = 8 * ((int64_t)threadIdx.x + 64 * W * p);
+            piece[p] = off < RB * ks ? *(const u32x2*)(ws + n0 * ks + off) : (u32x2){0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const int64_t row = n0 + r0 + u;
+          load_chunk<kNv, false, kNv>(wq, ws, row, kb, kval && row < n, khi, kq, ks, codes[u], sc[u]);
+        }
+        if (r0 == 0) {
+#pragma unroll
+          for (int p = 0; p < RB / 8; p++) {
+            const int off = 8 * (threadIdx.x + 64 * W * p);
+            if (off < RB * ks) *(u32x2*)&sblk[off] = piece[p];
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) sc[u] = kval ? (unsigned)sblk[(r0 + u) * ks + kr * 64 + lane] : 127u;
+      } else if (stage_sc) {
         const int rr = lane >> 3;
         const int64_t srow = n0 + r0 + rr;
         const uint8_t* sp = ws + (srow < n ? srow : 0) * ks + kr * SB + (SB / 8) * (lane & 7);

@@ -639,6 +639,20 @@ def test_gemv_ragged_shapes(n, k, m):
     mx_w4a16_case(w, x, f"w4a16 n={n} k={k} m={m}")
 
 
+# The vector-ALU decode kernel (m <= 4) on ragged row counts and k.
+# Blocks of 8 (m = 1) or 16 (m = 2..4) rows with one k range per wave
+# (6144 < k <= 8192, k % 256 == 0) stage their scale bytes block-wide; the
+# last, partial block and other k take the per-wave path.
+@pytest.mark.parametrize("n,k,m", [(1, 2048, 1), (3, 8192, 1), (7, 4096, 1), (4101, 6144, 1), (4097, 8192, 1),
+                                   (28673, 8192, 1), (70001, 2048, 1), (1000, 8192, 2), (517, 7424, 3),
+                                   (64, 6400, 4), (8, 7168, 1)])
+def test_gemv_m1_shapes(n, k, m):
+    rng = np.random.default_rng(n + k + m)
+    w = laplace_bf16(n * 3 + k, n, k, spread=10)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    mx_w4a16_case(w, x, f"m={m} {n}x{k}")
+
+
 # Shapes that reach the DMA-fed decode kernel (n >= 14336 rows, k a
 # multiple of 512, 2 <= m <= 64): one to eight 512-k stages against a three-
 # slot ring (4- and 16-row activation tiles), two to sixteen 256-k stages
