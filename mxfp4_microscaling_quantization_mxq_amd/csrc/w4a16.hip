@@ -526,16 +526,22 @@ __device__ __forceinline__ GSlot& g_slot() {
   return slot;
 }
 
-// NWV waves per block: 4 (2 x 2 wave tiles of 128 x 128, one wave per SIMD)
-// or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's MFMAs cover the
-// other's fragment reads, expansion and waits).
-template <bool kNv, bool kBf16Out, int NWV>
+// NWV waves per block in a WNR x (NWV / WNR) grid: 4 waves as 2 x 2 tiles
+// of 128 x 128 (one wave per SIMD), 8 as 2 x 4 of 128 x 64 (two waves per
+// SIMD, so one wave's MFMAs cover the other's fragment reads, expansion and
+// waits), or 8 as 1 x 8 of 256 x 32: every weight fragment then has a single
+// wave expanding it (in 2 x 4 the two waves of a SIMD expand the same
+// fragments), at twice the activation fragment reads -- the trade NVFP4's
+// per-element E4M3 multiply makes worthwhile.
+template <bool kNv, bool kBf16Out, int NWV, int WNR>
 __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
                                                        const float* __restrict__ gscale, int64_t n, int64_t k,
                                                        const uint16_t* __restrict__ x, int64_t m,
                                                        void* __restrict__ y) {
-  static_assert(NWV == 4 || NWV == 8, "4 or 8 waves");
-  constexpr int WNC = NWV / 2;         // wave columns
+  static_assert((NWV == 4 && WNR == 2) || (NWV == 8 && (WNR == 2 || WNR == 1)), "wave grid");
+  constexpr int WNC = NWV / WNR;       // wave columns
+  constexpr int WROWS = kGBM / WNR;    // activation rows per wave
+  constexpr int IA = WROWS / 32;       // activation fragments per wave
   constexpr int WCOLS = kGBN / WNC;    // weight rows (output columns) per wave
   constexpr int JB = WCOLS / 32;       // weight fragments per wave
   constexpr int RPW = kGBM / NWV;      // rows of x and of W each wave copies
@@ -605,14 +611,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
     }
   };
 
-  f32x16 acc[4][JB];
+  f32x16 acc[IA][JB];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < IA; i++)
 #pragma unroll
     for (int j = 0; j < JB; j++) acc[i][j] = (f32x16){};
 
   const int swz = (r32 >> 1) & 7;
-  const int laneX = (wm * 128 + r32) * 128;
+  const int laneX = (wm * WROWS + r32) * 128;
   const int laneW = (wn * WCOLS + r32) * 32 + ((half ^ ((r32 >> 3) & 1)) << 4);
 
   // weight operands of k step kk from the stage's code chunks: MXFP4 with
@@ -640,10 +646,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
       }
     }
   };
-  auto read_x = [&](const uint8_t* xb, int kk, bf16x8 xf[4]) {
+  auto read_x = [&](const uint8_t* xb, int kk, bf16x8 xf[IA]) {
     const int unit16 = ((4 * half + kk) ^ swz) << 4;
 #pragma unroll
-    for (int i = 0; i < 4; i++) xf[i] = *(const bf16x8*)(xb + laneX + i * 32 * 128 + unit16);
+    for (int i = 0; i < IA; i++) xf[i] = *(const bf16x8*)(xb + laneX + i * 32 * 128 + unit16);
   };
   // Software pipeline inside a stage (fixed by scheduling fences): the
   // activation fragments of step kk+1 are read and the weight operands of
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
     u32x4 wc[JB];
 #pragma unroll
     for (int j = 0; j < JB; j++) wc[j] = *(const u32x4*)(wb + laneW + j * 32 * 32);
-    bf16x8 xf[2][4], wf[2][JB];
+    bf16x8 xf[2][IA], wf[2][JB];
     read_x(xb, 0, xf[0]);
     dequant(wc, 0, sc, wf[0]);
 #pragma unroll
@@ -664,16 +670,19 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
       if (kk < 3) read_x(xb, kk + 1, xf[c ^ 1]);
       if (kk < 3) dequant(wc, kk + 1, sc, wf[c ^ 1]);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < IA; i++)
 #pragma unroll
         for (int j = 0; j < JB; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[c][j], xf[c][i], acc[i][j], 0, 0, 0);
       // reads first, then each MFMA followed by a share of the expansion
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      // (JB fragments of 8 weights per step, about 16 VALU each for NVFP4
+      // and 4-8 for MXFP4, spread over the IA x JB MFMAs)
+      constexpr int kVpm = IA == 4 ? (kNv ? 4 : 2) : (kNv ? 2 : 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, IA, 0);
 #pragma unroll
-      for (int g = 0; g < 4 * JB; g++) {
+      for (int g = 0; g < IA * JB; g++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kNv ? 4 : 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kVpm, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -724,8 +733,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
     // 16-byte units (8 columns): half 0 the units q = 0, 1, half 1 the units
     // q = 2, 3 (partial 8-byte stores wrote about 1.4x the output bytes)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t row = m0 + wm * 128 + i * 32 + r32;
+    for (int i = 0; i < IA; i++) {
+      const int64_t row = m0 + wm * WROWS + i * 32 + r32;
 #pragma unroll
       for (int j = 0; j < JB; j++) {
         u32x2 pk[4];
@@ -758,8 +767,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int64_t row = m0 + wm * 128 + i * 32 + r32;
+  for (int i = 0; i < IA; i++) {
+    const int64_t row = m0 + wm * WROWS + i * 32 + r32;
     if (row >= m) continue;
 #pragma unroll
     for (int j = 0; j < JB; j++) {
@@ -794,17 +803,25 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
 #define MXQ_W4A16_GEMM_WAVES 8
 #endif
 constexpr int kGemmWaves = MXQ_W4A16_GEMM_WAVES;
+// wave-grid rows: MXFP4 2 (2 x 4), NVFP4 1 (1 x 8)
+#ifndef MXQ_GEMM_WNR_MX
+#define MXQ_GEMM_WNR_MX 2
+#endif
+#ifndef MXQ_GEMM_WNR_NV
+#define MXQ_GEMM_WNR_NV 1
+#endif
 
 template <bool kNv>
 static void launch_gemm(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                         const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
+  constexpr int WNR = kGemmWaves == 4 ? 2 : (kNv ? MXQ_GEMM_WNR_NV : MXQ_GEMM_WNR_MX);
   const unsigned tiles = (unsigned)(((m + kGBM - 1) / kGBM) * ((n + kGBN - 1) / kGBN));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_gemm<kNv, true, kGemmWaves>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq, ws,
-                       gscale, n, k, (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, true, kGemmWaves, WNR>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq,
+                       ws, gscale, n, k, (const uint16_t*)x, m, y);
   else
-    hipLaunchKernelGGL((k_w4a16_gemm<kNv, false, kGemmWaves>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq, ws,
-                       gscale, n, k, (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_gemm<kNv, false, kGemmWaves, WNR>), dim3(tiles), dim3(64 * kGemmWaves), 0, st, wq,
+                       ws, gscale, n, k, (const uint16_t*)x, m, y);
 }
 
 template <bool kNv, int R, int U, int W>

@@ -729,7 +729,7 @@ def test_gemv_decode_full_size_sampled(m):
 
 def test_nv_gemm_ragged():
     for (n, k, m) in [(5, 16, 1), (40, 48, 3), (70, 272, 20), (256, 1024, 64), (300, 320, 130), (513, 64, 257),
-                      (264, 128, 136)]:
+                      (264, 128, 136), (700, 1088, 300), (1030, 4096, 513)]:
         w = laplace_bf16(n + k, n, k)
         x = synth.f32_to_bf16_bits(np.random.default_rng(k).standard_normal((m, k)).astype(np.float32))
         qo, so, go = assert_nv(w, None, f"nv gemm W {n}x{k}")
