@@ -71,16 +71,21 @@ extern "C" {
 
 #define MXQ_API __attribute__((visibility("default")))
 
+/* The *_MAX_ENUM members are never returned or accepted as valid; they give
+ * both enums the whole non-negative int range, so any int a caller passes
+ * (e.g. an unknown status code to mxq_status_string, or a bad dtype that
+ * validation rejects) is a value of the type. */
 typedef enum {
     MXQ_SUCCESS = 0,
     MXQ_ERROR_INVALID_VALUE = 1,
     MXQ_ERROR_MISALIGNED = 2,
     MXQ_ERROR_NOT_SUPPORTED = 3,
-    MXQ_ERROR_LAUNCH_FAILURE = 4
+    MXQ_ERROR_LAUNCH_FAILURE = 4,
+    MXQ_STATUS_MAX_ENUM = 0x7FFFFFFF
 } mxq_status;
 
 /* Element type of an unquantized operand: fp32, or bf16 (bfloat16). */
-typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1 } mxq_dtype;
+typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1, MXQ_DTYPE_MAX_ENUM = 0x7FFFFFFF } mxq_dtype;
 
 /* Static, NUL-terminated description of a status code (host memory). */
 MXQ_API const char *mxq_status_string(mxq_status s);

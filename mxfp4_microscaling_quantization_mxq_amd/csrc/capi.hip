@@ -62,6 +62,7 @@ const char* mxq_status_string(mxq_status s) {
     case MXQ_ERROR_MISALIGNED: return "misaligned pointer (16-byte alignment required)";
     case MXQ_ERROR_NOT_SUPPORTED: return "not supported (no HIP device, or the device is not gfx950)";
     case MXQ_ERROR_LAUNCH_FAILURE: return "kernel launch failed";
+    default: break;
   }
   return "unknown status";
 }

@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   constexpr int MTT = (MT + 15) / 16;                  // 16-row activation tiles
   constexpr int XPW = (MT / G::XRPI + NW - 1) / NW;    // activation copies per wave per stage
   constexpr int D = G::WC + G::SCP + XPW;              // copies per wave per stage
-  static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
+  static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 8 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
@@ -934,9 +934,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   for (int i = tid; i < G::XRowB / 16; i += 64 * NW) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     *(u32x4*)(dd_slot<MT, NW, KS, kNv, 0>().x + MT * G::XRowB + 16 * i) = z;
-    if (NR > 1) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 1 % NR>().x + MT * G::XRowB + 16 * i) = z;
-    if (NR > 2) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 2 % NR>().x + MT * G::XRowB + 16 * i) = z;
-    if (NR > 3) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 3 % NR>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 1) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 1>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 2) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 2>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 3) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 3>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 4) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 4>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 5) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 5>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 6) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 6>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 7) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 7>().x + MT * G::XRowB + 16 * i) = z;
   }
   __syncthreads();
 
@@ -1049,14 +1053,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   using I1 = std::integral_constant<int, 1 % NR>;
   using I2 = std::integral_constant<int, 2 % NR>;
   using I3 = std::integral_constant<int, 3 % NR>;
+  using I4 = std::integral_constant<int, 4 % NR>;
+  using I5 = std::integral_constant<int, 5 % NR>;
+  using I6 = std::integral_constant<int, 6 % NR>;
+  using I7 = std::integral_constant<int, 7 % NR>;
   issue(I0{}, 0);
-  if (NR > 2) issue(I1{}, 1);
-  if (NR > 3) issue(I2{}, 2);
+  if constexpr (NR > 2) issue(I1{}, 1);
+  if constexpr (NR > 3) issue(I2{}, 2);
+  if constexpr (NR > 4) issue(I3{}, 3);
+  if constexpr (NR > 5) issue(I4{}, 4);
+  if constexpr (NR > 6) issue(I5{}, 5);
+  if constexpr (NR > 7) issue(I6{}, 6);
   step(I0{}, 0);
   for (int s = 1; s < nst; s += NR) {
     step(I1{}, s);
-    if (NR > 2) step(I2{}, s + 1);
-    if (NR > 3) step(I3{}, s + 2);
+    if constexpr (NR > 2) step(I2{}, s + 1);
+    if constexpr (NR > 3) step(I3{}, s + 2);
+    if constexpr (NR > 4) step(I4{}, s + 3);
+    if constexpr (NR > 5) step(I5{}, s + 4);
+    if constexpr (NR > 6) step(I6{}, s + 5);
+    if constexpr (NR > 7) step(I7{}, s + 6);
     step(I0{}, s + NR - 1);
   }
   wait_vmcnt<0>();
@@ -1093,6 +1109,14 @@ static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float*
 }
 
 // Decode ring configurations <MT, NW, NR, KS> by activation rows.
+#ifndef MXQ_DD_KS4
+#define MXQ_DD_KS4 512
+#define MXQ_DD_NR4 3
+#endif
+#ifndef MXQ_DD_KS16
+#define MXQ_DD_KS16 512
+#define MXQ_DD_NR16 3
+#endif
 #ifndef MXQ_DD_KS32
 #define MXQ_DD_KS32 256
 #define MXQ_DD_NR32 4
@@ -1101,9 +1125,9 @@ template <bool kNv>
 static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                                const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   if (m <= 4)
-    launch_decode_dma<kNv, 4, 7, 3, 512>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+    launch_decode_dma<kNv, 4, 7, MXQ_DD_NR4, MXQ_DD_KS4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 16)
-    launch_decode_dma<kNv, 16, 7, 3, 512>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+    launch_decode_dma<kNv, 16, 7, MXQ_DD_NR16, MXQ_DD_KS16>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 32)
     launch_decode_dma<kNv, 32, 7, MXQ_DD_NR32, MXQ_DD_KS32>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 48)
