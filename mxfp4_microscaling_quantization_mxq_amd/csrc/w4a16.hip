@@ -1117,6 +1117,13 @@ static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float*
 #define MXQ_DD_KS16 512
 #define MXQ_DD_NR16 3
 #endif
+// NVFP4 at 5..16 rows: 256-k stages in a 5-slot ring, about 4 % faster than
+// the MXFP4 shape (measured on 28672 x 8192, m = 16: 41.0 vs 42.6 us); for
+// MXFP4 the shorter stages' extra barriers cost more (30.1 vs 26.6 us)
+#ifndef MXQ_DD_KS16_NV
+#define MXQ_DD_KS16_NV 256
+#define MXQ_DD_NR16_NV 5
+#endif
 #ifndef MXQ_DD_KS32
 #define MXQ_DD_KS32 256
 #define MXQ_DD_NR32 4
@@ -1126,6 +1133,8 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
                                const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   if (m <= 4)
     launch_decode_dma<kNv, 4, 7, MXQ_DD_NR4, MXQ_DD_KS4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  else if (m <= 16 && kNv)
+    launch_decode_dma<kNv, 16, 7, MXQ_DD_NR16_NV, MXQ_DD_KS16_NV>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 16)
     launch_decode_dma<kNv, 16, 7, MXQ_DD_NR16, MXQ_DD_KS16>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 32)

@@ -744,7 +744,7 @@ def test_nv_gemm_ragged():
 # NVFP4 weights at decode sizes: the staged-scale path of the m <= 4 kernel
 # (k % 256 == 0, whole 2048-k ranges; a partial last range and k % 32 == 16
 # take the byte-wise path), and the m = 4..64 ring kernel (n >= 14336,
-# k % 512 == 0; 512-k stages up to 16 rows, 256-k stages above; two passes
+# k % 512 == 0; 512-k stages up to 4 rows, 256-k stages above; two passes
 # for m = 65..128) with ragged weight rows.
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
                                    (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16), (14373, 512, 17),
