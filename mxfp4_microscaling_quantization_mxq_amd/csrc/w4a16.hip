@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
   // move half the bytes per request).  Block-uniform, so every wave meets
   // the barrier below exactly once.
   __shared__ __attribute__((aligned(16))) uint8_t sblk[kNv ? 16 : RB * 256];
-  const bool blk_sc = !kNv && U == 8 && RB % 8 == 0 && nkr == W && k % 256 == 0 && n0 + RB <= n;
+  const bool blk_sc = !kNv && U % 8 == 0 && RB % 8 == 0 && nkr == W && k % 256 == 0 && n0 + RB <= n;
 
   for (int64_t kr = wave; kr < nkr; kr += W) {
     const int64_t kb = kr * 2048 + 32 * lane;  // this lane's 32 k values
@@ -367,10 +367,15 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
   }
 }
 
+// m = 1: weight rows per block and rows whose loads a wave issues at once
+#ifndef MXQ_DV_RB1
+#define MXQ_DV_RB1 8
+#define MXQ_DV_U1 8
+#endif
 template <bool kNv, int M>
 static void launch_decode_valu(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                                const void* x, void* y, bool bf16_out, hipStream_t st) {
-  constexpr int RB = M == 1 ? 8 : 16, U = 8, W = 4;
+  constexpr int RB = M == 1 ? MXQ_DV_RB1 : 16, U = M == 1 ? MXQ_DV_U1 : 8, W = 4;
   dim3 grid((unsigned)((n + RB - 1) / RB));
   if (bf16_out)
     hipLaunchKernelGGL((k_w4a16_decode_valu<kNv, M, RB, U, W, true>), grid, dim3(64 * W), 0, st, wq, ws, gscale,

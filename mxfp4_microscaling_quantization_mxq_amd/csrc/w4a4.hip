@@ -114,6 +114,10 @@ __global__ __launch_bounds__(256) void k_w4a4_direct(const uint8_t* __restrict__
 }
 
 constexpr int kBM = 256;  // block tile rows of the ring kernel (columns: 256 or 128)
+// tile rows per group of the ring kernel's tile order (L2 reuse of B panels)
+#ifndef MXQ_W4A4_GROUP
+#define MXQ_W4A4_GROUP 4
+#endif
 
 // ---------------------------------------------------------------------------
 // Ring kernel (k % 1024 == 0).  Block tile 256 x 256; each wave multiplies
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   const int64_t tiles = tm_n * tn_n;
   int64_t tid_lin = blockIdx.x;
   if (tiles % 8 == 0) tid_lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
-  const int64_t group = 4;
+  const int64_t group = MXQ_W4A4_GROUP;
   const int64_t per_group = group * tn_n;
   const int64_t g0 = (tid_lin / per_group) * group;
   const int64_t gsz = (tm_n - g0) < group ? (tm_n - g0) : group;
