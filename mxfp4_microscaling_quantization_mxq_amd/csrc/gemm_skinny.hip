@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
     const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
     for (int q = 0; q < WC; q++)
-      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+      bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
     bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
     const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
 #pragma unroll
     for (int q = 0; q < WC; q++)
-      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+      bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
     bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * Slot::XRowB, sl.x + dx[j]);

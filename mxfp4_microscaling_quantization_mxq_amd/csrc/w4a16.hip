@@ -877,6 +877,8 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     a 28672 x 8192 weight).  The k order of a block's sum changes with
 //     its rotation; the result is still one fixed order per output row.
 //   * NVFP4: the tensor scale multiplies the fp32 sums in the epilogue.
+// Longest k whose scale rows the decode ring can keep resident in LDS.
+constexpr int kDdResK = 8192;
 // Stage geometry of the decode ring for KS k per stage (512 or 256).
 template <int KS, bool kNv>
 struct DdGeom {
@@ -899,31 +901,34 @@ struct DdGeom {
 // constant, so the compiler can tell that the reads of slot b do not touch
 // the slots whose copies are still in flight (one shared array would make it
 // wait for every outstanding copy before the first read).
-template <int MT, int NW, int KS, bool kNv>
+template <int MT, int NW, int KS, bool kNv, bool RS>
 struct DdSlot {
   using G = DdGeom<KS, kNv>;
   uint8_t w[16 * NW * G::RowB];
   uint8_t x[(MT + 1 + G::XRPI) * G::XRowB];  // MT activation rows, a zero row, scratch rows
-  uint8_t s[NW * G::SCP * 256];
+  uint8_t s[RS ? 16 : NW * G::SCP * 256];    // stage scales (resident scales: unused)
 };
-template <int MT, int NW, int KS, bool kNv, int B>
-__device__ __forceinline__ DdSlot<MT, NW, KS, kNv>& dd_slot() {
-  __shared__ __attribute__((aligned(1024))) DdSlot<MT, NW, KS, kNv> slot;
+// (16-byte alignment for the resident-scale rings, whose LDS is full to the
+// last KiB with NVFP4 scales: a uniform shift of a slot keeps its bank
+// pattern)
+template <int MT, int NW, int KS, bool kNv, bool RS, int B>
+__device__ __forceinline__ DdSlot<MT, NW, KS, kNv, RS>& dd_slot() {
+  __shared__ __attribute__((aligned(RS ? 16 : 1024))) DdSlot<MT, NW, KS, kNv, RS> slot;
   return slot;
 }
 
-template <bool kNv, int MT, int NW, int NR, int KS, bool kBf16Out>
+template <bool kNv, int MT, int NW, int NR, int KS, bool RS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* __restrict__ wq,
                                                                 const uint8_t* __restrict__ ws,
                                                                 const float* __restrict__ gscale, int64_t n,
                                                                 int64_t k, const uint16_t* __restrict__ x,
                                                                 int64_t m, void* __restrict__ y) {
   using G = DdGeom<KS, kNv>;
-  using Slot = DdSlot<MT, NW, KS, kNv>;
+  using Slot = DdSlot<MT, NW, KS, kNv, RS>;
   constexpr int RB = 16 * NW;                          // weight rows per block
   constexpr int MTT = (MT + 15) / 16;                  // 16-row activation tiles
   constexpr int XPW = (MT / G::XRPI + NW - 1) / NW;    // activation copies per wave per stage
-  constexpr int D = G::WC + G::SCP + XPW;              // copies per wave per stage
+  constexpr int D = G::WC + (RS ? 0 : G::SCP) + XPW;   // copies per wave per stage
   static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 8 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -934,18 +939,33 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   // staggered start, counted in 512-k chunks (the same k order for either
   // stage length)
   const int rot = (int)((blockIdx.x / 8) % (unsigned)(k / 512)) * (512 / KS);
+  // absolute stage of loop stage s (a stage past the end is clamped to the last)
+  auto stage_of = [&](int s) -> unsigned {
+    const int sl0 = min(s, nst - 1);
+    return (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+  };
+  // Resident scales (k <= kDdResK): the wave's 16 rows x ks scale bytes sit
+  // in LDS for the whole k loop, rows padded by 16 B (the 16 rows a fragment
+  // read touches then fall in distinct bank groups).  Per-stage scale copies
+  // were one 16- or 32-byte request per row and stage: about 6 % of the time
+  // at m = 4 and 11 % at m = 16 on a 28672 x 8192 weight.
+  constexpr int KSMAX = kNv ? kDdResK / 16 : kDdResK / 32;  // scale bytes per row, at most
+  constexpr int PU = KSMAX / 64;                            // 16-byte units per lane, at most
+  __shared__ __attribute__((aligned(16))) uint8_t sres[RS ? NW * 16 * (KSMAX + 16) : 16];
+  const int rsp = (int)ks + 16;                             // LDS pitch of a scale row
+  const int upr = (int)(ks >> 4);                           // 16-byte units per scale row
 
   // zero row (activation rows m..MT-1 of the MFMA operand read it)
   for (int i = tid; i < G::XRowB / 16; i += 64 * NW) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(dd_slot<MT, NW, KS, kNv, 0>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 1) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 1>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 2) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 2>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 3) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 3>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 4) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 4>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 5) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 5>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 6) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 6>().x + MT * G::XRowB + 16 * i) = z;
-    if constexpr (NR > 7) *(u32x4*)(dd_slot<MT, NW, KS, kNv, 7>().x + MT * G::XRowB + 16 * i) = z;
+    *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 0>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 1) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 1>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 2) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 2>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 3) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 3>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 4) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 4>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 5) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 5>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 6) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 6>().x + MT * G::XRowB + 16 * i) = z;
+    if constexpr (NR > 7) *(u32x4*)(dd_slot<MT, NW, KS, kNv, RS, 7>().x + MT * G::XRowB + 16 * i) = z;
   }
   __syncthreads();
 
@@ -982,16 +1002,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   const __amdgpu_buffer_rsrc_t rx = panel_rsrc(x, m * kx);
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    Slot& sl = dd_slot<MT, NW, KS, kNv, B>();
-    const int sl0 = min(s, nst - 1);
-    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+    Slot& sl = dd_slot<MT, NW, KS, kNv, RS, B>();
+    const unsigned sc = stage_of(s);
 #pragma unroll
     for (int q = 0; q < G::WC; q++)
-      bdma16(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
+      bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
     // LDS: piece h of the wave's rows at s + (SCP wave + h) * 256, row r of
     // the wave at + 16 r
+    if constexpr (!RS) {
 #pragma unroll
-    for (int h = 0; h < G::SCP; h++) bdma4(rs, offs + 16u * h, sc * G::ScB, sl.s + (G::SCP * wave + h) * 256);
+      for (int h = 0; h < G::SCP; h++) bdma4(rs, offs + 16u * h, sc * G::ScB, sl.s + (G::SCP * wave + h) * 256);
+    }
 #pragma unroll
     for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + xdst[j]);
   };
@@ -1000,16 +1021,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
 #pragma unroll
   for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int wrow = 16 * wave + col;  // this lane's block weight row
-  auto compute = [&](auto slot_tag) {
+  auto compute = [&](auto slot_tag, unsigned sc) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = dd_slot<MT, NW, KS, kNv, B>();
-    // this lane's row's scale bytes of the stage: ScB (E8M0 per 32 k or
-    // E4M3 per 16), word w = bytes 4w .. 4w+3
+    const Slot& sl = dd_slot<MT, NW, KS, kNv, RS, B>();
+    // this lane's row's scale bytes of the stage (absolute stage sc): ScB
+    // (E8M0 per 32 k or E4M3 per 16), word w = bytes 4w .. 4w+3
     unsigned svs[G::SCP * 4];
+    if constexpr (RS) {
+      const uint8_t* sp = sres + (16 * wave + col) * rsp + sc * G::ScB;
+      if constexpr (G::ScB >= 16) {
 #pragma unroll
-    for (int h = 0; h < G::SCP; h++) {
-      const u32x4 sv = *(const u32x4*)(sl.s + (G::SCP * wave + h) * 256 + 16 * col);
-      svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
+        for (int h = 0; h < G::SCP; h++) {
+          const u32x4 sv = *(const u32x4*)(sp + 16 * h);
+          svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
+        }
+      } else {
+        const u32x2 sv = *(const u32x2*)sp;
+        svs[0] = sv.x; svs[1] = sv.y; svs[2] = 0u; svs[3] = 0u;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G::SCP; h++) {
+        const u32x4 sv = *(const u32x4*)(sl.s + (G::SCP * wave + h) * 256 + 16 * col);
+        svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
+      }
     }
 #pragma unroll
     for (int i = 0; i < G::STEPS; i++) {
@@ -1048,7 +1083,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
-    if (s < nst) compute(slot_tag);
+    if (s < nst) compute(slot_tag, stage_of(s));
   };
 
   // prologue: stages 0 .. NR-2 in flight, then stage 0.  The loop below
@@ -1062,6 +1097,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   using I5 = std::integral_constant<int, 5 % NR>;
   using I6 = std::integral_constant<int, 6 % NR>;
   using I7 = std::integral_constant<int, 7 % NR>;
+  // resident scales: PU 16-byte loads per lane (unit i = lane + 64 p of the
+  // wave's 16 x ks bytes; units past the wave's rows re-read a valid unit
+  // and are dropped), issued before the ring's first copies
+  u32x4 rsv[RS ? PU : 1];
+  if constexpr (RS) {
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, c = i - r * upr;
+      const int row = min(16 * wave + min(r, 15), rows_w - 1);
+      rsv[p] = *(const u32x4*)(ws + (n0 + row) * ks + 16 * c);
+    }
+  }
   issue(I0{}, 0);
   if constexpr (NR > 2) issue(I1{}, 1);
   if constexpr (NR > 3) issue(I2{}, 2);
@@ -1069,6 +1117,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   if constexpr (NR > 5) issue(I4{}, 4);
   if constexpr (NR > 6) issue(I5{}, 5);
   if constexpr (NR > 7) issue(I6{}, 6);
+  if constexpr (RS) {
+    // the scale loads are older than the NR - 1 stages of copies in flight;
+    // only this wave reads its rows' scales, so no barrier is needed
+    wait_vmcnt<(NR - 1) * D>();
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, c = i - r * upr;
+      if (r < 16) *(u32x4*)(sres + (16 * wave + r) * rsp + 16 * c) = rsv[p];
+    }
+  }
   step(I0{}, 0);
   for (int s = 1; s < nst; s += NR) {
     step(I1{}, s);
@@ -1101,15 +1160,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   }
 }
 
-template <bool kNv, int MT, int NW, int NR, int KS>
+template <bool kNv, int MT, int NW, int NR, int KS, bool RS = false>
 static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                               const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, wq, ws, gscale,
-                       n, k, (const uint16_t*)x, m, y);
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, RS, true>), grid, dim3(64 * NW), 0, st, wq, ws,
+                       gscale, n, k, (const uint16_t*)x, m, y);
   else
-    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, wq, ws,
+    hipLaunchKernelGGL((k_w4a16_decode_dma<kNv, MT, NW, NR, KS, RS, false>), grid, dim3(64 * NW), 0, st, wq, ws,
                        gscale, n, k, (const uint16_t*)x, m, y);
 }
 
@@ -1122,9 +1181,10 @@ static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float*
 #define MXQ_DD_KS16 512
 #define MXQ_DD_NR16 3
 #endif
-// NVFP4 at 5..16 rows: 256-k stages in a 5-slot ring, about 4 % faster than
-// the MXFP4 shape (measured on 28672 x 8192, m = 16: 41.0 vs 42.6 us); for
-// MXFP4 the shorter stages' extra barriers cost more (30.1 vs 26.6 us)
+// Stage-scale rings (k > kDdResK).  NVFP4 at 5..16 rows: 256-k stages in a
+// 5-slot ring, about 4 % faster than the MXFP4 shape (measured on 28672 x
+// 8192, m = 16: 41.0 vs 42.6 us); for MXFP4 the shorter stages' scale
+// copies cost more (30.1 vs 26.6 us)
 #ifndef MXQ_DD_KS16_NV
 #define MXQ_DD_KS16_NV 256
 #define MXQ_DD_NR16_NV 5
@@ -1133,10 +1193,37 @@ static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float*
 #define MXQ_DD_KS32 256
 #define MXQ_DD_NR32 4
 #endif
+// Resident-scale rings (k <= kDdResK) for up to 16 activation rows: up to 4
+// rows keep the 512-k, 3-slot ring; 5..16 rows take 256-k stages in a
+// 4-slot ring (ring and resident scales fit in LDS).  Measured on 28672 x
+// 8192: MXFP4 m = 16 24.7 us against 26.7 us for the 512-k ring with stage
+// scale copies and 29.1 us for the same 256-k ring with stage scale copies
+// (8 bytes per row and stage); NVFP4 m = 16 39.3 against 40.7 us (5 slots,
+// stage copies); m = 4 unchanged (24.2 vs 24.0 us).
+#ifndef MXQ_DD_RS
+#define MXQ_DD_RS 1
+#endif
+#ifndef MXQ_DD_RS4
+#define MXQ_DD_RS4 3, 512
+#endif
+#ifndef MXQ_DD_RS16
+#define MXQ_DD_RS16 4, 256
+#endif
+#ifndef MXQ_DD_RS16_NV
+#define MXQ_DD_RS16_NV 4, 256
+#endif
 template <bool kNv>
 static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                                const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  if (m <= 4)
+  const bool res = MXQ_DD_RS && k <= kDdResK;
+  if (m <= 16 && res) {
+    if (m <= 4)
+      launch_decode_dma<kNv, 4, 7, MXQ_DD_RS4, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+    else if constexpr (kNv)
+      launch_decode_dma<kNv, 16, 7, MXQ_DD_RS16_NV, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+    else
+      launch_decode_dma<kNv, 16, 7, MXQ_DD_RS16, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+  } else if (m <= 4)
     launch_decode_dma<kNv, 4, 7, MXQ_DD_NR4, MXQ_DD_KS4>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   else if (m <= 16 && kNv)
     launch_decode_dma<kNv, 16, 7, MXQ_DD_NR16_NV, MXQ_DD_KS16_NV>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);

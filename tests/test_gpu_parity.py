@@ -654,8 +654,9 @@ def test_gemv_m1_shapes(n, k, m):
 
 
 # Shapes that reach the DMA-fed decode kernel (n >= 14336 rows, k a
-# multiple of 512, 2 <= m <= 64): one to eight 512-k stages against a three-
-# slot ring (4- and 16-row activation tiles), two to sixteen 256-k stages
+# multiple of 512, 2 <= m <= 64): up to 16 rows with resident scale rows
+# (k <= 8192: 512-k stages for 4-row tiles, 256-k stages for 16-row tiles)
+# and with per-stage scale copies (k > 8192), two to sixteen 256-k stages
 # against a four-slot ring (32-row tiles) and a three-slot ring (64-row
 # tiles), row tails that leave part of the last block empty, and activation
 # counts on both sides of every tile height; m = 65..128 runs as a 64-row pass
@@ -663,7 +664,8 @@ def test_gemv_m1_shapes(n, k, m):
 @pytest.mark.parametrize("n,k,m", [(14336, 512, 2), (14373, 1024, 3), (14447, 1536, 4), (14400, 2048, 5),
                                    (14336, 2560, 16), (15000, 1536, 12), (14336, 4096, 2), (14336, 512, 17),
                                    (14373, 1536, 32), (14400, 4096, 33), (14447, 1024, 48), (14336, 2560, 64),
-                                   (15000, 512, 64), (14336, 1024, 65), (14373, 1536, 100), (14400, 512, 128)])
+                                   (15000, 512, 64), (14336, 1024, 65), (14373, 1536, 100), (14400, 512, 128),
+                                   (14336, 8704, 4), (14373, 9216, 16)])
 def test_gemv_decode_dma_shapes(n, k, m):
     w = laplace_bf16(n + 7 * k + m, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(100 + m).standard_normal((m, k)).astype(np.float32))
@@ -749,7 +751,7 @@ def test_nv_gemm_ragged():
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
                                    (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16), (14373, 512, 17),
                                    (14400, 1536, 32), (14336, 2560, 40), (14447, 1024, 64),
-                                   (14373, 512, 66), (14400, 1024, 128)])
+                                   (14373, 512, 66), (14400, 1024, 128), (14336, 8704, 4), (14373, 9216, 9)])
 def test_nv_decode_paths(n, k, m):
     w = laplace_bf16(n + 3 * k + m, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(k + m).standard_normal((m, k)).astype(np.float32))
