@@ -75,37 +75,39 @@ __device__ __forceinline__ int skinny_rotation(int64_t k) {
 // One ring slot.  Each slot is its own LDS variable and every slot index is
 // a compile-time constant, so the compiler can tell that reads of one slot
 // do not touch the slots whose copies are in flight.
-template <int MT, int NW, int KS, bool kFp8>
+template <int MT, int NW, int KS, bool kFp8, bool RS>
 struct SkSlot {
   using G = SkGeom<KS, kFp8>;
   uint8_t w[16 * NW * G::RowB];          // weight codes
   uint8_t x[(MT + G::XRPI) * G::XRowB];  // activation codes, one copy's worth of scratch rows
   // Scales: a 256-byte region per 16 rows (one 64-lane dword copy), row r
   // of a group at (r % 16) * ScB; with 8 scale bytes per row the upper half
-  // of a region is scratch.
-  uint8_t ws[NW * 256];                  // weight scales
-  uint8_t xs[(MT / 16 + 1) * 256];       // activation scales, one scratch region
+  // of a region is scratch.  (Resident scale rows: unused.)
+  uint8_t ws[RS ? 16 : NW * 256];                // weight scales
+  uint8_t xs[RS ? 16 : (MT / 16 + 1) * 256];     // activation scales, one scratch region
 };
-template <int MT, int NW, int KS, bool kFp8, int B>
-__device__ __forceinline__ SkSlot<MT, NW, KS, kFp8>& sk_slot() {
-  __shared__ __attribute__((aligned(1024))) SkSlot<MT, NW, KS, kFp8> slot;
+template <int MT, int NW, int KS, bool kFp8, bool RS, int B>
+__device__ __forceinline__ SkSlot<MT, NW, KS, kFp8, RS>& sk_slot() {
+  __shared__ __attribute__((aligned(1024))) SkSlot<MT, NW, KS, kFp8, RS> slot;
   return slot;
 }
+// Longest k whose scale rows the ring keeps resident in LDS.
+constexpr int kSkResK = 8192;
 
-template <bool kFp8, int MT, int NW, int NR, int KS, bool kBf16Out>
+template <bool kFp8, int MT, int NW, int NR, int KS, bool RS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
                                                            const uint8_t* __restrict__ bq,
                                                            const uint8_t* __restrict__ bs, int64_t m,
                                                            int64_t n, int64_t k, void* __restrict__ c) {
   using G = SkGeom<KS, kFp8>;
-  using Slot = SkSlot<MT, NW, KS, kFp8>;
+  using Slot = SkSlot<MT, NW, KS, kFp8, RS>;
   constexpr int RB = 16 * NW;                        // weight rows per block
   constexpr int MTT = MT / 16;                       // 16-row activation tiles
   constexpr int WC = 16 / G::RPI;                    // weight code copies per wave
   constexpr int XC = (MT / G::XRPI + NW - 1) / NW;   // activation code copies per wave
   constexpr int XS = (MT / 16 + NW - 1) / NW;        // activation scale copies per wave (16 rows each)
-  constexpr int D = WC + 1 + XC + XS;                // copies per wave per stage
+  constexpr int D = WC + (RS ? 0 : 1 + XS) + XC;     // copies per wave per stage
   constexpr int WSW = swz(G::U), XSW = swz(G::XU);   // swizzle periods
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -115,6 +117,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   const int64_t kq = k / 2, ks = k / 32, kx = kFp8 ? k : k / 2;
   const int nst = (int)(k / KS);
   const int rot = skinny_rotation<KS>(k);
+  // absolute stage of loop stage s (a stage past the end is clamped to the last)
+  auto stage_of = [&](int s) -> unsigned {
+    const int sl0 = min(s, nst - 1);
+    return (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+  };
+  // Resident scale rows (k <= kSkResK, at most 16 activation rows): each
+  // wave's 16 weight rows x ks E8M0 bytes and the block's MT activation rows
+  // x ks sit in LDS for the whole k loop, rows padded by 16 B (a fragment
+  // read's 16 rows fall in distinct bank groups), instead of two small
+  // per-stage scale copies.
+  static_assert(!RS || MT <= 16, "resident activation scales: one 16-row tile");
+  constexpr int KSMAX = kSkResK / 32;                // scale bytes per row, at most
+  constexpr int PU = KSMAX / 64;                     // 16-byte units per lane (weight rows), at most
+  __shared__ __attribute__((aligned(16))) uint8_t wres[RS ? NW * 16 * (KSMAX + 16) : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xres[RS ? MT * (KSMAX + 16) : 16];
+  const int rsp = (int)ks + 16;                      // LDS pitch of a scale row
+  const int upr = (int)(ks >> 4);                    // 16-byte units per scale row
 
   // Lane offsets of the copies, fixed for the whole k loop (a stage only
   // moves the uniform offset).  Rows past the operand are clamped to its
@@ -158,17 +177,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   // the same copies.
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    Slot& sl = sk_slot<MT, NW, KS, kFp8, B>();
-    const int sl0 = min(s, nst - 1);
-    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+    Slot& sl = sk_slot<MT, NW, KS, kFp8, RS, B>();
+    const unsigned sc = stage_of(s);
 #pragma unroll
     for (int q = 0; q < WC; q++)
       bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
-    bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
+    if constexpr (!RS) bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
+    if constexpr (!RS) {
 #pragma unroll
-    for (int j = 0; j < XS; j++) bdma4(rxs, offxs[j], sc * G::ScB, sl.xs + dxs[j]);
+      for (int j = 0; j < XS; j++) bdma4(rxs, offxs[j], sc * G::ScB, sl.xs + dxs[j]);
+    }
   };
 
   f32x4 acc[MTT];
@@ -196,13 +216,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
       return (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     }
   };
-  auto compute = [&](auto slot_tag) {
+  auto compute = [&](auto slot_tag, unsigned sc) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = sk_slot<MT, NW, KS, kFp8, B>();
+    const Slot& sl = sk_slot<MT, NW, KS, kFp8, RS, B>();
     unsigned wss[G::STEPS], xss[MTT][G::STEPS];
-    scale_words(sl.ws + 256 * wave + col * G::ScB, wss);
+    if constexpr (RS) {
+      scale_words(wres + wrow * rsp + sc * G::ScB, wss);
 #pragma unroll
-    for (int t = 0; t < MTT; t++) scale_words(sl.xs + 256 * t + col * G::ScB, xss[t]);
+      for (int t = 0; t < MTT; t++) scale_words(xres + (16 * t + col) * rsp + sc * G::ScB, xss[t]);
+    } else {
+      scale_words(sl.ws + 256 * wave + col * G::ScB, wss);
+#pragma unroll
+      for (int t = 0; t < MTT; t++) scale_words(sl.xs + 256 * t + col * G::ScB, xss[t]);
+    }
 #pragma unroll
     for (int i = 0; i < G::STEPS; i++) {
       const int wslot = ((4 * i + g) ^ (col % WSW)) << 4;  // weight unit 4i+g of a row r, r % 16 == col
@@ -228,16 +254,43 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
-    if (s < nst) compute(slot_tag);
+    if (s < nst) compute(slot_tag, stage_of(s));
   };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1 % NR>;
   using I2 = std::integral_constant<int, 2 % NR>;
   using I3 = std::integral_constant<int, 3 % NR>;
+  // resident scales: PU loads per lane of the wave's weight scale rows
+  // (units past its 16 rows re-read a valid unit and are dropped) and one
+  // load per thread of the activation scale rows, before the ring's copies
+  u32x4 wsv[RS ? PU : 1], xsv = {0u, 0u, 0u, 0u};
+  if constexpr (RS) {
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, cu = i - r * upr;
+      const int row = min(16 * wave + min(r, 15), rows_w - 1);
+      wsv[p] = *(const u32x4*)(bs + (n0 + row) * ks + 16 * cu);
+    }
+    const int r = min(tid / upr, MT - 1), cu = tid - (tid / upr) * upr;
+    xsv = *(const u32x4*)(as + min((int64_t)r, m - 1) * ks + 16 * cu);
+  }
   issue(I0{}, 0);
   if (NR > 2) issue(I1{}, 1);
   if (NR > 3) issue(I2{}, 2);
+  if constexpr (RS) {
+    // the scale loads are older than the NR - 1 stages of copies in flight;
+    // the first stage's barrier publishes the activation scales
+    wait_vmcnt<(NR - 1) * D>();
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, cu = i - r * upr;
+      if (r < 16) *(u32x4*)(wres + (16 * wave + r) * rsp + 16 * cu) = wsv[p];
+    }
+    if (tid < MT * upr) *(u32x4*)(xres + (tid / upr) * rsp + 16 * (tid - (tid / upr) * upr)) = xsv;
+  }
   step(I0{}, 0);
   for (int s = 1; s < nst; s += NR) {
     step(I1{}, s);
@@ -264,16 +317,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   }
 }
 
-template <bool kFp8, int MT, int NW, int NR, int KS>
+template <bool kFp8, int MT, int NW, int NR, int KS, bool RS = false>
 static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                       int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs, m,
-                       n, k, c);
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, RS, true>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs,
+                       m, n, k, c);
   else
-    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs, m,
-                       n, k, c);
+    hipLaunchKernelGGL((k_gemm_skinny<kFp8, MT, NW, NR, KS, RS, false>), grid, dim3(64 * NW), 0, st, aq, as, bq, bs,
+                       m, n, k, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,9 +589,26 @@ bool gemm_skinny_applies(int64_t m, int64_t k) {
   return m >= 1 && m <= 128 && k >= 512 && k % 512 == 0 && k <= (1 << 24);
 }
 
+// Up to 16 activation rows with k <= kSkResK: resident scale rows, 256-k
+// stages in a 4-slot ring.  Measured on a 28672 x 8192 weight, m = 16
+// (interleaved A/B): W4A4 21.8 us against 22.4 us with per-stage scale
+// copies (512-k, 3 slots) and 21.9 us resident with 512-k stages; W4A8 21.9
+// against 23.3 and 22.1 us.
+#ifndef MXQ_SK_RS
+#define MXQ_SK_RS 1
+#endif
+#ifndef MXQ_SK4_RS16
+#define MXQ_SK4_RS16 16, 7, 4, 256
+#endif
+#ifndef MXQ_SK8_RS16
+#define MXQ_SK8_RS16 16, 7, 4, 256
+#endif
+
 hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
                               int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  if (m <= 16)
+  if (m <= 16 && MXQ_SK_RS && k <= kSkResK)
+    launch_sk<false, MXQ_SK4_RS16, true>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 16)
     launch_sk<false, MXQ_SK4_C16>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
   else if (m <= 32)
     launch_sk<false, MXQ_SK4_C32>(aq, as, bq, bs, m, n, k, c, bf16_out, st);
@@ -551,7 +621,9 @@ hipError_t launch_w4a4_skinny(const uint8_t* aq, const uint8_t* as, const uint8_
 
 hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
                               int64_t m, int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  if (m <= 16)
+  if (m <= 16 && MXQ_SK_RS && k <= kSkResK)
+    launch_sk<true, MXQ_SK8_RS16, true>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
+  else if (m <= 16)
     launch_sk<true, MXQ_SK8_C16>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
   else if (m <= 32)
     launch_sk<true, MXQ_SK8_C32>(aq8, as, bq, bs, m, n, k, c, bf16_out, st);
