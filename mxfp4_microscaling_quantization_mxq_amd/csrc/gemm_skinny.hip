@@ -347,18 +347,18 @@ static void launch_sk(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, c
 //     the kernel above for the same m: the product is bit-identical to
 //     quantize-then-GEMM (mxq_quantize + mxq_gemm_w4a4, or
 //     mxq_quantize_fp8 + mxq_gemm_w4a8).
-template <int MT, int NW, int KS>
+template <int MT, int NW, int KS, bool RS>
 struct SkDynSlot {
   using G = SkGeom<KS, false>;
   static constexpr int XRowB = 2 * KS;        // bf16 bytes per activation row
   static constexpr int XRPI = 1024 / XRowB;   // activation rows per 1-KiB copy (1 or 2)
   uint8_t w[16 * NW * G::RowB];               // weight codes
   uint8_t x[(MT + XRPI) * XRowB];             // bf16 activation rows, one copy's worth of scratch
-  uint8_t ws[NW * 256];                       // weight scales (256-byte region per 16 rows)
+  uint8_t ws[RS ? 16 : NW * 256];             // weight scales (256-byte region per 16 rows)
 };
-template <int MT, int NW, int KS, int B>
-__device__ __forceinline__ SkDynSlot<MT, NW, KS>& sk_dyn_slot() {
-  __shared__ __attribute__((aligned(1024))) SkDynSlot<MT, NW, KS> slot;
+template <int MT, int NW, int KS, bool RS, int B>
+__device__ __forceinline__ SkDynSlot<MT, NW, KS, RS>& sk_dyn_slot() {
+  __shared__ __attribute__((aligned(1024))) SkDynSlot<MT, NW, KS, RS> slot;
   return slot;
 }
 template <int MT, int KS, bool kFp8>
@@ -374,19 +374,19 @@ __device__ __forceinline__ SkDynTile<MT, KS, kFp8>& sk_dyn_tile() {
   return tile;
 }
 
-template <bool kFp8, int MT, int NW, int NR, int KS, bool kBf16Out>
+template <bool kFp8, int MT, int NW, int NR, int KS, bool RS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* __restrict__ x,
                                                               const uint8_t* __restrict__ bq,
                                                               const uint8_t* __restrict__ bs, int64_t m,
                                                               int64_t n, int64_t k, void* __restrict__ c) {
   using G = SkGeom<KS, kFp8>;
-  using Slot = SkDynSlot<MT, NW, KS>;
+  using Slot = SkDynSlot<MT, NW, KS, RS>;
   constexpr int RB = 16 * NW;                         // weight rows per block
   constexpr int MTT = MT / 16;                        // 16-row activation tiles
   constexpr int WC = 16 / G::RPI;                     // weight code copies per wave
   constexpr int XU = Slot::XRowB / 16;                // 16-byte units per bf16 row
   constexpr int XC = (MT / Slot::XRPI + NW - 1) / NW; // activation copies per wave
-  constexpr int D = WC + 1 + XC;                      // copies per wave per stage
+  constexpr int D = WC + (RS ? 0 : 1) + XC;           // copies per wave per stage
   constexpr int BPR = KS / 32;                        // MX blocks per row per stage
   constexpr int NB = MT * BPR;                        // MX blocks per stage
   constexpr int QPL = (NB + 64 * NW - 1) / (64 * NW); // blocks each lane quantizes
@@ -399,6 +399,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   const int64_t kq = k / 2, ks = k / 32, kx = 2 * k;
   const int nst = (int)(k / KS);
   const int rot = skinny_rotation<KS>(k);
+  auto stage_of = [&](int s) -> unsigned {
+    const int sl0 = min(s, nst - 1);
+    return (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+  };
+  // resident weight scale rows (k <= kSkResK), as in k_gemm_skinny
+  constexpr int KSMAX = kSkResK / 32;
+  constexpr int PU = KSMAX / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t wres[RS ? NW * 16 * (KSMAX + 16) : 16];
+  const int rsp = (int)ks + 16;
+  const int upr = (int)(ks >> 4);
 
   unsigned offw[WC], offx[XC];
   int dx[XC];
@@ -423,13 +433,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
 
   auto issue = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
-    const int sl0 = min(s, nst - 1);
-    const unsigned sc = (unsigned)(sl0 + rot < nst ? sl0 + rot : sl0 + rot - nst);
+    Slot& sl = sk_dyn_slot<MT, NW, KS, RS, B>();
+    const unsigned sc = stage_of(s);
 #pragma unroll
     for (int q = 0; q < WC; q++)
       bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
-    bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
+    if constexpr (!RS) bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
     for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * Slot::XRowB, sl.x + dx[j]);
   };
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   SkDynTile<MT, KS, kFp8>& tile = sk_dyn_tile<MT, KS, kFp8>();
   auto quantize = [&](auto slot_tag) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
+    const Slot& sl = sk_dyn_slot<MT, NW, KS, RS, B>();
 #pragma unroll
     for (int j = 0; j < QPL; j++) {
       const int q = tid + 64 * NW * j;
@@ -465,9 +474,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
 #pragma unroll
   for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int wrow = 16 * wave + col;
-  auto compute = [&](auto slot_tag) {
+  auto compute = [&](auto slot_tag, unsigned sc) {
     constexpr int B = decltype(slot_tag)::value;
-    const Slot& sl = sk_dyn_slot<MT, NW, KS, B>();
+    const Slot& sl = sk_dyn_slot<MT, NW, KS, RS, B>();
     unsigned wss[G::STEPS], xss[MTT][G::STEPS];
     auto words = [&](const uint8_t* p, unsigned (&wds)[G::STEPS]) {
       if constexpr (G::STEPS == 4) {
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
         wds[0] = v.x; wds[1] = v.y;
       }
     };
-    words(sl.ws + 256 * wave + col * G::ScB, wss);
+    words(RS ? wres + wrow * rsp + sc * G::ScB : sl.ws + 256 * wave + col * G::ScB, wss);
 #pragma unroll
     for (int t = 0; t < MTT; t++) words(tile.xs + 256 * t + col * G::ScB, xss[t]);
 #pragma unroll
@@ -519,7 +528,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
       quantize(slot_tag);
       __builtin_amdgcn_s_waitcnt((15 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
-      compute(slot_tag);
+      compute(slot_tag, stage_of(s));
     }
   };
 
@@ -527,9 +536,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   using I1 = std::integral_constant<int, 1 % NR>;
   using I2 = std::integral_constant<int, 2 % NR>;
   using I3 = std::integral_constant<int, 3 % NR>;
+  u32x4 wsv[RS ? PU : 1];
+  if constexpr (RS) {
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, cu = i - r * upr;
+      const int row = min(16 * wave + min(r, 15), rows_w - 1);
+      wsv[p] = *(const u32x4*)(bs + (n0 + row) * ks + 16 * cu);
+    }
+  }
   issue(I0{}, 0);
   if (NR > 2) issue(I1{}, 1);
   if (NR > 3) issue(I2{}, 2);
+  if constexpr (RS) {
+    // older than the NR - 1 stages of copies in flight; only this wave
+    // reads its rows' scales
+    wait_vmcnt<(NR - 1) * D>();
+#pragma unroll
+    for (int p = 0; p < PU; p++) {
+      const int i = lane + 64 * p;
+      const int r = i / upr, cu = i - r * upr;
+      if (r < 16) *(u32x4*)(wres + (16 * wave + r) * rsp + 16 * cu) = wsv[p];
+    }
+  }
   step(I0{}, 0);
   for (int s = 1; s < nst; s += NR) {
     step(I1{}, s);
@@ -634,16 +664,16 @@ hipError_t launch_w4a8_skinny(const uint8_t* aq8, const uint8_t* as, const uint8
   return hipGetLastError();
 }
 
-template <bool kFp8, int MT, int NW, int NR, int KS>
+template <bool kFp8, int MT, int NW, int NR, int KS, bool RS = false>
 static void launch_skd(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n, int64_t k,
                        void* c, bool bf16_out, hipStream_t st) {
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)));
   if (bf16_out)
-    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, true>), grid, dim3(64 * NW), 0, st, x, bq, bs, m, n,
-                       k, c);
-  else
-    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, false>), grid, dim3(64 * NW), 0, st, x, bq, bs, m,
+    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, RS, true>), grid, dim3(64 * NW), 0, st, x, bq, bs, m,
                        n, k, c);
+  else
+    hipLaunchKernelGGL((k_dynamic_skinny<kFp8, MT, NW, NR, KS, RS, false>), grid, dim3(64 * NW), 0, st, x, bq, bs,
+                       m, n, k, c);
 }
 
 // Up to 16 activation rows.  Measured on a 28672 x 8192 weight against
@@ -653,9 +683,19 @@ static void launch_skd(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, 
 // at m = 16, 38.6-42.0 vs 29.2-29.6 us at m = 32.  Every block pulls a
 // bf16 tile (4x the bytes of MXFP4 codes, 2x those of MXFP8) through the
 // same copy path as the weights.
+// W4A4, k <= kSkResK: resident weight scale rows, 256-k stages in 4 slots
+// (m = 16 on a 28672 x 8192 weight: 23.2-23.5 against 24.9 us).  The same
+// shape made W4A8 slower (26.3 against 24.8 us), which keeps 512-k stages
+// with per-stage scale copies.
+#ifndef MXQ_SKD_RS16
+#define MXQ_SKD_RS16 16, 7, 4, 256
+#endif
 hipError_t launch_w4a4_dynamic(const uint16_t* x, const uint8_t* bq, const uint8_t* bs, int64_t m, int64_t n,
                                int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  launch_skd<false, 16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
+  if (MXQ_SK_RS && k <= kSkResK)
+    launch_skd<false, MXQ_SKD_RS16, true>(x, bq, bs, m, n, k, c, bf16_out, st);
+  else
+    launch_skd<false, 16, 7, 3, 512>(x, bq, bs, m, n, k, c, bf16_out, st);
   return hipGetLastError();
 }
 
