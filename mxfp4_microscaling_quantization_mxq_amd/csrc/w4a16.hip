@@ -946,9 +946,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   };
   // Resident scales (k <= kDdResK): the wave's 16 rows x ks scale bytes sit
   // in LDS for the whole k loop, rows padded by 16 B (the 16 rows a fragment
-  // read touches then fall in distinct bank groups).  Per-stage scale copies
-  // were one 16- or 32-byte request per row and stage: about 6 % of the time
-  // at m = 4 and 11 % at m = 16 on a 28672 x 8192 weight.
+  // read touches then fall in distinct bank groups), instead of per-stage
+  // copies of one 8-, 16- or 32-byte request per row and stage.  They make
+  // the shorter 256-k stages pay at m = 16 (launch_decode_ring has the
+  // figures).
   constexpr int KSMAX = kNv ? kDdResK / 16 : kDdResK / 32;  // scale bytes per row, at most
   constexpr int PU = KSMAX / 64;                            // 16-byte units per lane, at most
   __shared__ __attribute__((aligned(16))) uint8_t sres[RS ? NW * 16 * (KSMAX + 16) : 16];
