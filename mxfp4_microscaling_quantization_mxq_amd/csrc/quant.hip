@@ -22,16 +22,50 @@ namespace mxq {
 // The block absmax is an integer max over magnitude bits, shared inside the
 // quad with two DPP steps; the E8M0 exponent floor(log2 amax) - 2 is read
 // straight off the exponent field.
+// A block takes kQuantU chunks of 256 lanes and issues all their loads
+// before any arithmetic (more bytes in flight per wave); lanes past the end
+// re-read the first chunk's lane and store nothing.  nlanes is a multiple
+// of 4 and chunks are 256 lanes, so quads stay whole.
+// Chunks per block, measured (interleaved A/B against one chunk per block)
+// on the dynamic-quantize tensor 16384 x 8192 bf16 and an 8192 x 8192 one:
+// MXFP4 54.9 -> 52.4 us with 2 (53.2 with 4); MXFP8 35.7 -> 32.8 us with 4
+// (33.3 with 2); rotated MXFP4 (hk 32) 61.9 -> 52.7 us with 4 (55.2 with
+// 2); NVFP4 quantize pass of the 8192 x 4096 weight: 31.7 -> 30.9 us.
+#ifndef MXQ_QUANT_U
+#define MXQ_QUANT_U 2
+#endif
+#ifndef MXQ_QUANT8_U
+#define MXQ_QUANT8_U 4
+#endif
+#ifndef MXQ_HAD_U
+#define MXQ_HAD_U 4
+#endif
+#ifndef MXQ_NVQ_U
+#define MXQ_NVQ_U 2
+#endif
+constexpr int kQuantU = MXQ_QUANT_U, kQuant8U = MXQ_QUANT8_U, kHadU = MXQ_HAD_U, kNvqU = MXQ_NVQ_U;
 __global__ __launch_bounds__(256) void k_mx_quantize_bf16(const u32x4* __restrict__ x,
                                                           unsigned* __restrict__ q,
                                                           uint8_t* __restrict__ s,
                                                           int64_t nlanes) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;  // nlanes is a multiple of 4: quads stay whole
-  const bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
-  unsigned code;
-  q[t] = mx_quantize_quad_bf16(xb, &code);
-  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kQuantU) + threadIdx.x;
+  if (t0 >= nlanes) return;
+  bf16x8 xb[kQuantU];
+#pragma unroll
+  for (int u = 0; u < kQuantU; u++) {
+    const int64_t t = t0 + 256 * u;
+    xb[u] = __builtin_nontemporal_load((const bf16x8*)&x[t < nlanes ? t : t0]);
+  }
+#pragma unroll
+  for (int u = 0; u < kQuantU; u++) {
+    const int64_t t = t0 + 256 * u;
+    unsigned code;
+    const unsigned out = mx_quantize_quad_bf16(xb[u], &code);
+    if (t < nlanes) {
+      q[t] = out;
+      if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_mx_quantize_f32(const u32x4* __restrict__ x,
@@ -102,15 +136,28 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void k_mx8_quantize_bf16(const u32x4* __restrict__ x, u32x2* __restrict__ q,
                                                            uint8_t* __restrict__ s, int64_t nlanes) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;  // quads stay whole
-  const bf16x8 xb = __builtin_nontemporal_load((const bf16x8*)&x[t]);
-  unsigned m = bf16x8_absmax_bits(xb);
-  m = max(m, dpp_quad_xor1(m));
-  m = max(m, dpp_quad_xor2(m));
-  const unsigned code = e8m0_code_e4m3(m >> 7);
-  q[t] = mx8_encode8_bf16(xb, code);
-  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+  // kQuant8U chunks of 256 lanes per block, loads first (as k_mx_quantize_bf16)
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kQuant8U) + threadIdx.x;
+  if (t0 >= nlanes) return;  // quads stay whole
+  bf16x8 xb[kQuant8U];
+#pragma unroll
+  for (int u = 0; u < kQuant8U; u++) {
+    const int64_t t = t0 + 256 * u;
+    xb[u] = __builtin_nontemporal_load((const bf16x8*)&x[t < nlanes ? t : t0]);
+  }
+#pragma unroll
+  for (int u = 0; u < kQuant8U; u++) {
+    const int64_t t = t0 + 256 * u;
+    unsigned m = bf16x8_absmax_bits(xb[u]);
+    m = max(m, dpp_quad_xor1(m));
+    m = max(m, dpp_quad_xor2(m));
+    const unsigned code = e8m0_code_e4m3(m >> 7);
+    const u32x2 out = mx8_encode8_bf16(xb[u], code);
+    if (t < nlanes) {
+      q[t] = out;
+      if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_mx8_quantize_f32(const u32x4* __restrict__ x, u32x2* __restrict__ q,
@@ -231,29 +278,40 @@ template <bool kBf16In, int HK>
 __global__ __launch_bounds__(256) void k_mx_quantize_hadamard(const u32x4* __restrict__ x, unsigned* __restrict__ q,
                                                               uint8_t* __restrict__ s, int64_t nlanes) {
   static_assert(HK == 16 || HK == 32 || HK == 64 || HK == 128, "rotation size");
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // nlanes is a multiple of HK / 8 and of 4, and blocks hold 256 lanes:
-  // rotation groups and MXFP4 quads are whole or absent
-  if (t >= nlanes) return;
+  // kHadU chunks of 256 lanes per block, loads first (as k_mx_quantize_bf16).
+  // nlanes is a multiple of HK / 8 and of 4, and chunks hold 256 lanes:
+  // rotation groups and MXFP4 quads are whole, valid or past the end
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kHadU) + threadIdx.x;
+  if (t0 >= nlanes) return;
   const int lane = threadIdx.x & 63;
-  float v[8];
-  load8<kBf16In>(x, t, v);
-  rotate8<HK>(v, lane);
-  // MXFP4 of the rotated block (as k_mx_quantize_f32)
-  unsigned m = 0;
+  float v[kHadU][8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-  m = max(m, dpp_quad_xor1(m));
-  m = max(m, dpp_quad_xor2(m));
-  const unsigned code = e8m0_code_from_expfield(m >> 23);
-  const float scale = e8m0_as_scale(code);
-  unsigned out = 0;
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], scale, 0);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], scale, 1);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], scale, 2);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], scale, 3);
-  q[t] = out;
-  if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+  for (int u = 0; u < kHadU; u++) {
+    const int64_t t = t0 + 256 * u;
+    load8<kBf16In>(x, t < nlanes ? t : t0, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kHadU; u++) {
+    const int64_t t = t0 + 256 * u;
+    rotate8<HK>(v[u], lane);
+    // MXFP4 of the rotated block (as k_mx_quantize_f32)
+    unsigned m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
+    m = max(m, dpp_quad_xor1(m));
+    m = max(m, dpp_quad_xor2(m));
+    const unsigned code = e8m0_code_from_expfield(m >> 23);
+    const float scale = e8m0_as_scale(code);
+    unsigned out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[u][0], v[u][1], scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[u][2], v[u][3], scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[u][4], v[u][5], scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[u][6], v[u][7], scale, 3);
+    if (t < nlanes) {
+      q[t] = out;
+      if ((t & 3) == 0) s[t >> 2] = (uint8_t)code;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- NVFP4
@@ -349,59 +407,57 @@ template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_nv_quantize(const u32x4* __restrict__ x, const float* __restrict__ g,
                                                      unsigned* __restrict__ q, uint8_t* __restrict__ s,
                                                      int64_t nlanes) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;  // nlanes is even: pairs stay whole
+  // kNvqU chunks of 256 lanes per block, loads first (as k_mx_quantize_bf16);
+  // nlanes is even and chunks hold 256 lanes: pairs stay whole
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kNvqU) + threadIdx.x;
+  if (t0 >= nlanes) return;
   const float st = *g;
-  float xs[8];
-  unsigned m;
-  if (kBf16In) {
-    u32x4 v = __builtin_nontemporal_load(&x[t]);
-    unsigned w[4] = {v.x, v.y, v.z, v.w};
+  float xv[kNvqU][8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      xs[2 * i] = __uint_as_float(w[i] << 16);
-      xs[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    u32x4 a = __builtin_nontemporal_load(&x[2 * t]);
-    u32x4 b = __builtin_nontemporal_load(&x[2 * t + 1]);
-    unsigned w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; i++) xs[i] = __uint_as_float(w[i]);
+  for (int u = 0; u < kNvqU; u++) {
+    const int64_t t = t0 + 256 * u;
+    load8<kBf16In>(x, t < nlanes ? t : t0, xv[u]);
   }
-  m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(xs[i]) & 0x7FFFFFFFu);
-  m = max(m, dpp_quad_xor1(m));
-  float tden = 6.0f * st;
-  unsigned sb = e4m3_encode_nonneg(__fdiv_rn(__uint_as_float(m), tden));
-  float sbv = e4m3_value(sb);
-  unsigned out = 0;
-  if (sbv == 0.0f) {
+  for (int u = 0; u < kNvqU; u++) {
+    const int64_t t = t0 + 256 * u;
+    const float (&xs)[8] = xv[u];
+    unsigned m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) out |= (__float_as_uint(xs[i]) >> 31) << (3 + 4 * i);
-  } else {
-    const float d = st * sbv;
-    float v[8];
-    if (d >= 0x1p-100f && __uint_as_float(m) <= d * 0x1p100f) {
-      const float y = __fdiv_rn(1.0f, d);
+    for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(xs[i]) & 0x7FFFFFFFu);
+    m = max(m, dpp_quad_xor1(m));
+    float tden = 6.0f * st;
+    unsigned sb = e4m3_encode_nonneg(__fdiv_rn(__uint_as_float(m), tden));
+    float sbv = e4m3_value(sb);
+    unsigned out = 0;
+    if (sbv == 0.0f) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const unsigned xb = __float_as_uint(xs[i]);
-        const float aq = div_by_block_scale(__uint_as_float(xb & 0x7FFFFFFFu), d, y);
-        v[i] = __uint_as_float(__float_as_uint(aq) | (xb & 0x80000000u));
-      }
+      for (int i = 0; i < 8; i++) out |= (__float_as_uint(xs[i]) >> 31) << (3 + 4 * i);
     } else {
+      const float d = st * sbv;
+      float v[8];
+      if (d >= 0x1p-100f && __uint_as_float(m) <= d * 0x1p100f) {
+        const float y = __fdiv_rn(1.0f, d);
 #pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = __fdiv_rn(xs[i], d);
+        for (int i = 0; i < 8; i++) {
+          const unsigned xb = __float_as_uint(xs[i]);
+          const float aq = div_by_block_scale(__uint_as_float(xb & 0x7FFFFFFFu), d, y);
+          v[i] = __uint_as_float(__float_as_uint(aq) | (xb & 0x80000000u));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = __fdiv_rn(xs[i], d);
+      }
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], 1.0f, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], 1.0f, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], 1.0f, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], 1.0f, 3);
     }
-    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], 1.0f, 0);
-    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], 1.0f, 1);
-    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], 1.0f, 2);
-    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], 1.0f, 3);
+    if (t < nlanes) {
+      q[t] = out;
+      if ((t & 1) == 0) s[t >> 1] = (uint8_t)sb;
+    }
   }
-  q[t] = out;
-  if ((t & 1) == 0) s[t >> 1] = (uint8_t)sb;
 }
 
 // NVFP4 dequantize: y = s_t * (s_b * q).  s_b * q is exact in fp32 (at most
@@ -668,6 +724,13 @@ __global__ __launch_bounds__(256) void k_tf4_quantize(const u32x4* __restrict__ 
 // Dequantize: y_hat = fl(c * fl(s_t * E4M3(s_b))) with the codebook the tag
 // selects, the residual added at its position, then x_hat = H^T y_hat = H
 // y_hat (H_32 is symmetric and orthonormal) in the same butterfly order.
+// 256-lane chunks per block, loads issued together (16384 x 8192: 128 us
+// with one chunk and the residual loaded after the meta byte, 95 us with
+// one chunk and every load up front, 74.6 with 2, 70.7 with 4, 80.7 with 8)
+#ifndef MXQ_TF4D_U
+#define MXQ_TF4D_U 4
+#endif
+constexpr int kTf4dU = MXQ_TF4D_U;
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void k_tf4_dequantize(const unsigned* __restrict__ q,
                                                         const uint8_t* __restrict__ s,
@@ -675,48 +738,66 @@ __global__ __launch_bounds__(256) void k_tf4_dequantize(const unsigned* __restri
                                                         const uint16_t* __restrict__ res,
                                                         const float* __restrict__ g, void* __restrict__ y,
                                                         int64_t nlanes) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kTf4dU) + threadIdx.x;
+  if (t0 >= nlanes) return;  // nlanes % 4 == 0 and chunks are 256 lanes: quads stay whole
   const int lane = threadIdx.x & 63;
-  const unsigned c = q[t];
-  const float d = *g * e4m3_value(s[t >> 1]);
-  const unsigned mb = meta[t >> 2];
-  const int at = (int)(mb & 31u);
-  float v[8];
-  if (mb & 0x80u) {
+  // every load of the block's kTf4dU chunks up front, none depending on
+  // another (the residual used to be loaded only by the lane holding its
+  // position, once the meta byte had arrived: two memory round trips in a
+  // row).  Lanes past the end read lane 0's bytes and store nothing.
+  const float st = *g;
+  unsigned c[kTf4dU], sbyte[kTf4dU], mb[kTf4dU], rbits[kTf4dU];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const unsigned ci = (c >> (4 * i)) & 15u;
-      const float mag = (float)(ci & 7u);
-      v[i] = (ci & 8u) ? -mag : mag;
+  for (int u = 0; u < kTf4dU; u++) {
+    const int64_t t = t0 + 256 * u < nlanes ? t0 + 256 * u : 0;
+    c[u] = q[t];
+    sbyte[u] = s[t >> 1];
+    mb[u] = meta[t >> 2];
+    rbits[u] = res[t >> 2];
+  }
+#pragma unroll
+  for (int u = 0; u < kTf4dU; u++) {
+    const int64_t t = t0 + 256 * u;
+    const float d = st * e4m3_value(sbyte[u]);
+    const int at = (int)(mb[u] & 31u);
+    float v[8];
+    if (mb[u] & 0x80u) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const unsigned ci = (c[u] >> (4 * i)) & 15u;
+        const float mag = (float)(ci & 7u);
+        v[i] = (ci & 8u) ? -mag : mag;
+      }
+    } else {
+      const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u], 1.0f, 0);
+      const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u], 1.0f, 1);
+      const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u], 1.0f, 2);
+      const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[u], 1.0f, 3);
+      v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+      v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
     }
-  } else {
-    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
-    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
-    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
-    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
-  }
 #pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = v[i] * d;
-  if ((at >> 3) == (lane & 3)) {
-    const float rv = __uint_as_float((unsigned)res[t >> 2] << 16);
+    for (int i = 0; i < 8; i++) v[i] = v[i] * d;
+    {
+      const bool own = (at >> 3) == (lane & 3);
+      const float rv = __uint_as_float(rbits[u] << 16);
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-      if ((at & 7) == i) v[i] = v[i] + rv;
-  }
-  rotate8<32>(v, lane);
-  if (kBf16Out) {
-    u32x4 o;
-    o.x = f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
-    o.y = f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
-    o.z = f32_to_bf16_rne(v[4]) | ((unsigned)f32_to_bf16_rne(v[5]) << 16);
-    o.w = f32_to_bf16_rne(v[6]) | ((unsigned)f32_to_bf16_rne(v[7]) << 16);
-    ((u32x4*)y)[t] = o;
-  } else {
-    ((f32x4*)y)[2 * t] = (f32x4){v[0], v[1], v[2], v[3]};
-    ((f32x4*)y)[2 * t + 1] = (f32x4){v[4], v[5], v[6], v[7]};
+      for (int i = 0; i < 8; i++) v[i] = own && (at & 7) == i ? v[i] + rv : v[i];
+    }
+    rotate8<32>(v, lane);
+    if (t < nlanes) {
+      if (kBf16Out) {
+        u32x4 o;
+        o.x = f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16);
+        o.y = f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16);
+        o.z = f32_to_bf16_rne(v[4]) | ((unsigned)f32_to_bf16_rne(v[5]) << 16);
+        o.w = f32_to_bf16_rne(v[6]) | ((unsigned)f32_to_bf16_rne(v[7]) << 16);
+        ((u32x4*)y)[t] = o;
+      } else {
+        ((f32x4*)y)[2 * t] = (f32x4){v[0], v[1], v[2], v[3]};
+        ((f32x4*)y)[2 * t + 1] = (f32x4){v[4], v[5], v[6], v[7]};
+      }
+    }
   }
 }
 
@@ -728,8 +809,8 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
                               hipStream_t st) {
   int64_t nlanes = rows * k / 8;
   if (bf16)
-    hipLaunchKernelGGL(k_mx_quantize_bf16, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
-                       (unsigned*)q, s, nlanes);
+    hipLaunchKernelGGL(k_mx_quantize_bf16, dim3(grid_for(nlanes, 256 * kQuantU)), dim3(256), 0, st,
+                       (const u32x4*)x, (unsigned*)q, s, nlanes);
   else
     hipLaunchKernelGGL(k_mx_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
                        (unsigned*)q, s, nlanes);
@@ -740,8 +821,8 @@ hipError_t launch_mx8_quantize(const void* x, bool bf16, int64_t rows, int64_t k
                                hipStream_t st) {
   const int64_t nlanes = rows * k / 8;
   if (bf16)
-    hipLaunchKernelGGL(k_mx8_quantize_bf16, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
-                       (u32x2*)q, s, nlanes);
+    hipLaunchKernelGGL(k_mx8_quantize_bf16, dim3(grid_for(nlanes, 256 * kQuant8U)), dim3(256), 0, st,
+                       (const u32x4*)x, (u32x2*)q, s, nlanes);
   else
     hipLaunchKernelGGL(k_mx8_quantize_f32, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
                        (u32x2*)q, s, nlanes);
@@ -752,10 +833,10 @@ template <int HK>
 static void launch_mx_quantize_hadamard_hk(const void* x, bool bf16, int64_t nlanes, uint8_t* q, uint8_t* s,
                                            hipStream_t st) {
   if (bf16)
-    hipLaunchKernelGGL((k_mx_quantize_hadamard<true, HK>), dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_mx_quantize_hadamard<true, HK>), dim3(grid_for(nlanes, 256 * kHadU)), dim3(256), 0, st,
                        (const u32x4*)x, (unsigned*)q, s, nlanes);
   else
-    hipLaunchKernelGGL((k_mx_quantize_hadamard<false, HK>), dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_mx_quantize_hadamard<false, HK>), dim3(grid_for(nlanes, 256 * kHadU)), dim3(256), 0, st,
                        (const u32x4*)x, (unsigned*)q, s, nlanes);
 }
 
@@ -801,10 +882,10 @@ hipError_t launch_nv_quantize(const void* x, bool bf16, int64_t rows, int64_t k,
     hipLaunchKernelGGL(k_nv_scale, dim3(1), dim3(kScaleThreads), 0, st, (const unsigned*)part, np, gscale);
   }
   if (bf16)
-    hipLaunchKernelGGL(k_nv_quantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+    hipLaunchKernelGGL(k_nv_quantize<true>, dim3(grid_for(nlanes, 256 * kNvqU)), dim3(256), 0, st, (const u32x4*)x,
                        (const float*)gscale, (unsigned*)q, s, nlanes);
   else
-    hipLaunchKernelGGL(k_nv_quantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const u32x4*)x,
+    hipLaunchKernelGGL(k_nv_quantize<false>, dim3(grid_for(nlanes, 256 * kNvqU)), dim3(256), 0, st, (const u32x4*)x,
                        (const float*)gscale, (unsigned*)q, s, nlanes);
   return hipGetLastError();
 }
@@ -848,12 +929,13 @@ hipError_t launch_tf4_dequantize(const uint8_t* q, const uint8_t* s, const uint8
                                  const float* gscale, int64_t rows, int64_t k, void* y, bool bf16_out,
                                  hipStream_t st) {
   const int64_t nlanes = rows * k / 8;
+  const dim3 grid(grid_for(nlanes, 256 * kTf4dU));
   if (bf16_out)
-    hipLaunchKernelGGL(k_tf4_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const unsigned*)q, s,
-                       meta, res, gscale, y, nlanes);
+    hipLaunchKernelGGL(k_tf4_dequantize<true>, grid, dim3(256), 0, st, (const unsigned*)q, s, meta, res, gscale, y,
+                       nlanes);
   else
-    hipLaunchKernelGGL(k_tf4_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st, (const unsigned*)q,
-                       s, meta, res, gscale, y, nlanes);
+    hipLaunchKernelGGL(k_tf4_dequantize<false>, grid, dim3(256), 0, st, (const unsigned*)q, s, meta, res, gscale, y,
+                       nlanes);
   return hipGetLastError();
 }
 
