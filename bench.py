@@ -189,6 +189,15 @@ def main():
                     rotating([(q, s_, m, r, g, y) for (x, q, s_, m, r, g), y in zip(tsets, ydq)],
                              lambda q, s_, m, r, g, y: mxq.transfp4_dequantize(q, s_, m, r, g, y=y)),
                     tf4_bytes + 2 * ntf, 0, "hbm"))
+        # MXFP4 dequantize of the same tensor back to bf16 (codes and scales
+        # of the plain quantize above)
+        dsets = []
+        for (x, q, s_), y in zip(sets, ydq):
+            q2, s2 = torch.empty_like(q), torch.empty_like(s_)
+            mxq.quantize(x, q2, s2)
+            dsets.append((q2, s2, y))
+        ops.append(("dequantize_16384x8192_bf16", rotating(dsets, lambda q, s_, y: mxq.dequantize(q, s_, y=y)),
+                    ntf // 2 + ntf // 32 + 2 * ntf, 0, "hbm"))
     if "gemv" in parts:
         n2, k2 = 28672, 8192
         w2, _ = synth.decode_gemv(1)

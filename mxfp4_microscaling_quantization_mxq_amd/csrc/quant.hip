@@ -92,30 +92,50 @@ __global__ __launch_bounds__(256) void k_mx_quantize_f32(const u32x4* __restrict
 }
 
 // Dequantize: one lane = 4 code bytes = 8 elements, scale byte t/4.
+// kDeqU chunks of 256 lanes per block with every load issued first (a
+// lane's own loads are 4 code bytes and a scale byte: one chunk per thread
+// left the loads' latency exposed).  16384 x 8192 to bf16: MXFP4 62.3 ->
+// 60.2 us, NVFP4 83.8 -> 60.1 us (8 chunks: 63.7 and 65.3 us).
+#ifndef MXQ_DEQ_U
+#define MXQ_DEQ_U 4
+#endif
+constexpr int kDeqU = MXQ_DEQ_U;
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void k_mx_dequantize(const unsigned* __restrict__ q,
                                                        const uint8_t* __restrict__ s,
                                                        void* __restrict__ y, int64_t nlanes) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;
-  unsigned c = q[t];
-  float scale = e8m0_as_scale(s[t >> 2]);
-  if (kBf16Out) {
-    u32x4 o;
-    o.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
-    o.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
-    o.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
-    o.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
-    ((u32x4*)y)[t] = o;
-  } else {
-    auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 0);
-    auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 1);
-    auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 2);
-    auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 3);
-    f32x4 o0 = {p0[0], p0[1], p1[0], p1[1]};
-    f32x4 o1 = {p2[0], p2[1], p3[0], p3[1]};
-    ((f32x4*)y)[2 * t] = o0;
-    ((f32x4*)y)[2 * t + 1] = o1;
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kDeqU) + threadIdx.x;
+  if (t0 >= nlanes) return;
+  unsigned cv[kDeqU], sv[kDeqU];
+#pragma unroll
+  for (int u = 0; u < kDeqU; u++) {
+    const int64_t t = t0 + 256 * u < nlanes ? t0 + 256 * u : t0;
+    cv[u] = q[t];
+    sv[u] = s[t >> 2];
+  }
+#pragma unroll
+  for (int u = 0; u < kDeqU; u++) {
+    const int64_t t = t0 + 256 * u;
+    if (t >= nlanes) break;
+    const unsigned c = cv[u];
+    const float scale = e8m0_as_scale(sv[u]);
+    if (kBf16Out) {
+      u32x4 o;
+      o.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
+      o.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
+      o.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
+      o.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
+      ((u32x4*)y)[t] = o;
+    } else {
+      auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 0);
+      auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 1);
+      auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 2);
+      auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 3);
+      f32x4 o0 = {p0[0], p0[1], p1[0], p1[1]};
+      f32x4 o1 = {p2[0], p2[1], p3[0], p3[1]};
+      ((f32x4*)y)[2 * t] = o0;
+      ((f32x4*)y)[2 * t + 1] = o1;
+    }
   }
 }
 
@@ -469,33 +489,46 @@ __global__ __launch_bounds__(256) void k_nv_dequantize(const unsigned* __restric
                                                        const uint8_t* __restrict__ s,
                                                        const float* __restrict__ g, void* __restrict__ y,
                                                        int64_t nlanes) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nlanes) return;
-  float st = *g;
-  unsigned c = q[t];
-  float sbv = e4m3_value(s[t >> 1]);
-  auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-  auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
-  auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
-  auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-  const float r[8] = {p0[0] * sbv, p0[1] * sbv, p1[0] * sbv, p1[1] * sbv,
-                      p2[0] * sbv, p2[1] * sbv, p3[0] * sbv, p3[1] * sbv};
-  if (kBf16Out) {
-    unsigned short h[8];
+  // kDeqU chunks of 256 lanes per block, loads first (as k_mx_dequantize)
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kDeqU) + threadIdx.x;
+  if (t0 >= nlanes) return;
+  const float st = *g;
+  unsigned cv[kDeqU], sv[kDeqU];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      float p = st * r[i];
-      float e = __builtin_fmaf(st, r[i], -p);
-      h[i] = bf16_rne_of_sum(p, e);
+  for (int u = 0; u < kDeqU; u++) {
+    const int64_t t = t0 + 256 * u < nlanes ? t0 + 256 * u : t0;
+    cv[u] = q[t];
+    sv[u] = s[t >> 1];
+  }
+#pragma unroll
+  for (int u = 0; u < kDeqU; u++) {
+    const int64_t t = t0 + 256 * u;
+    if (t >= nlanes) break;
+    const unsigned c = cv[u];
+    const float sbv = e4m3_value(sv[u]);
+    auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    const float r[8] = {p0[0] * sbv, p0[1] * sbv, p1[0] * sbv, p1[1] * sbv,
+                        p2[0] * sbv, p2[1] * sbv, p3[0] * sbv, p3[1] * sbv};
+    if (kBf16Out) {
+      unsigned short h[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        float p = st * r[i];
+        float e = __builtin_fmaf(st, r[i], -p);
+        h[i] = bf16_rne_of_sum(p, e);
+      }
+      u32x4 o = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
+                 h[6] | ((unsigned)h[7] << 16)};
+      ((u32x4*)y)[t] = o;
+    } else {
+      f32x4 o0 = {st * r[0], st * r[1], st * r[2], st * r[3]};
+      f32x4 o1 = {st * r[4], st * r[5], st * r[6], st * r[7]};
+      ((f32x4*)y)[2 * t] = o0;
+      ((f32x4*)y)[2 * t + 1] = o1;
     }
-    u32x4 o = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16), h[4] | ((unsigned)h[5] << 16),
-               h[6] | ((unsigned)h[7] << 16)};
-    ((u32x4*)y)[t] = o;
-  } else {
-    f32x4 o0 = {st * r[0], st * r[1], st * r[2], st * r[3]};
-    f32x4 o1 = {st * r[4], st * r[5], st * r[6], st * r[7]};
-    ((f32x4*)y)[2 * t] = o0;
-    ((f32x4*)y)[2 * t + 1] = o1;
   }
 }
 
@@ -857,10 +890,10 @@ hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows
                                 bool bf16, hipStream_t st) {
   int64_t nlanes = rows * k / 8;
   if (bf16)
-    hipLaunchKernelGGL(k_mx_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_mx_dequantize<true>, dim3(grid_for(nlanes, 256 * kDeqU)), dim3(256), 0, st,
                        (const unsigned*)q, s, y, nlanes);
   else
-    hipLaunchKernelGGL(k_mx_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_mx_dequantize<false>, dim3(grid_for(nlanes, 256 * kDeqU)), dim3(256), 0, st,
                        (const unsigned*)q, s, y, nlanes);
   return hipGetLastError();
 }
@@ -894,10 +927,10 @@ hipError_t launch_nv_dequantize(const uint8_t* q, const uint8_t* s, const float*
                                 int64_t k, void* y, bool bf16, hipStream_t st) {
   int64_t nlanes = rows * k / 8;
   if (bf16)
-    hipLaunchKernelGGL(k_nv_dequantize<true>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_nv_dequantize<true>, dim3(grid_for(nlanes, 256 * kDeqU)), dim3(256), 0, st,
                        (const unsigned*)q, s, gscale, y, nlanes);
   else
-    hipLaunchKernelGGL(k_nv_dequantize<false>, dim3(grid_for(nlanes, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_nv_dequantize<false>, dim3(grid_for(nlanes, 256 * kDeqU)), dim3(256), 0, st,
                        (const unsigned*)q, s, gscale, y, nlanes);
   return hipGetLastError();
 }
