@@ -62,18 +62,15 @@ __device__ __forceinline__ float e8m0_value(unsigned code) {
 }
 
 // E4M3 (OCP FP8) value of a code: S EEEE MMM, bias 7, subnormals for
-// E = 0, and S 1111 111 is NaN.
-__device__ __forceinline__ float e4m3_value(unsigned c) {
-  unsigned e = (c >> 3) & 15u, m = c & 7u;
-  float v;
-  if (e == 0)
-    v = (float)m * 0x1p-9f;  // subnormal: m/8 * 2^-6
-  else if (e == 15u && m == 7u)
-    v = __builtin_nanf("");
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -v : v;
+// E = 0 (m/8 * 2^-6), and S 1111 111 is NaN.  gfx950's fp8 convert decodes
+// exactly this format (OCP, not the FNUZ variant of earlier CDNA parts) in
+// one instruction; the exhaustive dequantize test holds it to the oracle's
+// field decode for every code.  B selects byte B of the word.
+template <int B = 0>
+__device__ __forceinline__ float e4m3_value_b(unsigned w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
 }
+__device__ __forceinline__ float e4m3_value(unsigned c) { return e4m3_value_b<0>(c); }
 
 // E4M3 encode of r >= 0 (finite or +Inf): round to nearest, ties to even
 // mantissa, saturate at 448, underflow to 0.

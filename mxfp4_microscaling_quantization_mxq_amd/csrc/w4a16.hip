@@ -42,7 +42,7 @@ __device__ __forceinline__ void dequant_chunk(u32x4 c, unsigned sbytes, bf16x8 w
     }
   } else {
     // two E4M3 block scales: k 0..15 and k 16..31 of the chunk
-    float s0 = e4m3_value(sbytes & 0xFFu), s1 = e4m3_value((sbytes >> 8) & 0xFFu);
+    const float s0 = e4m3_value_b<0>(sbytes), s1 = e4m3_value_b<1>(sbytes);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       float sb = j < 2 ? s0 : s1;
@@ -334,8 +334,8 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
             for (int i = 0; i < 8; i++) p0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p0, false);
 #pragma unroll
             for (int i = 8; i < 16; i++) p1 = __builtin_amdgcn_fdot2_f32_bf16(w[i], xs[mm][i], p1, false);
-            acc = __builtin_fmaf(p0, e4m3_value(sc[u] & 0xFFu), acc);
-            acc = __builtin_fmaf(p1, e4m3_value((sc[u] >> 8) & 0xFFu), acc);
+            acc = __builtin_fmaf(p0, e4m3_value_b<0>(sc[u]), acc);
+            acc = __builtin_fmaf(p1, e4m3_value_b<1>(sc[u]), acc);
           }
           red[wave][mm][r0 + u][lane] = acc;
         }
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a16_gemm(const uint8_t* __res
         bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
         wf[j] = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       } else {
-        const float sb = e4m3_value(kk < 2 ? (sc[j] & 0xFFu) : ((sc[j] >> 8) & 0xFFu));
+        const float sb = kk < 2 ? e4m3_value_b<0>(sc[j]) : e4m3_value_b<1>(sc[j]);
         auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
         auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
         auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);

@@ -594,6 +594,28 @@ def test_nv_quantize_c5_full_size():
     assert_nv(x, None, "C5 X 4096x4096")
 
 
+def test_nv_dequantize_every_byte_and_scale():
+    # rows = E4M3 block-scale codes 0..255 (subnormal, negative and both NaN
+    # codes included); each row holds all 256 code bytes.  With s_t = 1 the
+    # value s_b * q is exact in fp32 and in bf16; with s_t = 0.3 the fp32
+    # output is the single rounding of the exact product.
+    q = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    s = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 16, axis=1)
+    for gs, dts in [(1.0, (torch.float32, torch.bfloat16)), (0.3, (torch.float32,))]:
+        gs32 = float(np.float32(gs))
+        ref = oracle.nv_dequantize(q, s, gs32)
+        gd = torch.tensor([gs32], dtype=torch.float32, device="cuda")
+        for dt in dts:
+            out = host(mxq.nv_dequantize(dev(q), dev(s), gd, dt))
+            if dt == torch.float32:
+                got, exp = out, ref.astype(np.float32)
+            else:
+                got, exp = bf16_bits_to_f64(out).astype(np.float32), f64_to_bf16_rne(ref).astype(np.float32)
+            same = (got == exp) & (np.signbit(got) == np.signbit(exp))
+            same |= np.isnan(got) & np.isnan(exp)
+            assert same.all(), f"s_t {gs} {dt}: {np.argwhere(~same)[:5].tolist()}"
+
+
 def test_nv_dequantize_rounds_once():
     xf = laplace_f32(77, 64, 256, spread=20)
     q, s, g = oracle.nv_quantize(xf)
