@@ -1031,8 +1031,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     // this lane's row's scale bytes of the stage (absolute stage sc): ScB
     // (E8M0 per 32 k or E4M3 per 16), word w = bytes 4w .. 4w+3
     unsigned svs[G::SCP * 4];
-    if constexpr (RS) {
-      const uint8_t* sp = sres + (16 * wave + col) * rsp + sc * G::ScB;
+    const uint8_t* sp = sres + (16 * wave + col) * rsp + sc * G::ScB;
+    if constexpr (RS && kNv) {
+      // read per chunk below: the two bytes of lane group g's chunk sit at a
+      // lane-dependent offset, and one 2-byte LDS read replaces selecting
+      // them out of the stage's words
+    } else if constexpr (RS) {
       if constexpr (G::ScB >= 16) {
 #pragma unroll
         for (int h = 0; h < G::SCP; h++) {
@@ -1054,8 +1058,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     for (int i = 0; i < G::STEPS; i++) {
       const u32x4 cw = *(const u32x4*)(sl.w + wrow * G::RowB + (((4 * i + g) ^ (col % G::U)) << 4));
       bf16x8 wf[4];
-      if constexpr (kNv) {
+      if constexpr (kNv && RS) {
         // the two E4M3 scales of chunk 4i + g: bytes 8i + 2g, 8i + 2g + 1
+        dequant_chunk<true>(cw, *(const uint16_t*)(sp + 8 * i + 2 * g), wf);
+      } else if constexpr (kNv) {
         dequant_chunk<true>(cw, (svs[2 * i + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu, wf);
       } else {
         dequant_chunk<false>(cw, (svs[i] >> (8 * g)) & 0xFFu, wf);
