@@ -773,7 +773,8 @@ def test_nv_gemm_ragged():
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
                                    (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16), (14373, 512, 17),
                                    (14400, 1536, 32), (14336, 2560, 40), (14447, 1024, 64),
-                                   (14373, 512, 66), (14400, 1024, 128), (14336, 8704, 4), (14373, 9216, 9)])
+                                   (14373, 512, 66), (14400, 1024, 128), (14336, 8704, 4), (14373, 9216, 9),
+                                   (14447, 8192, 13), (14400, 7680, 4)])
 def test_nv_decode_paths(n, k, m):
     w = laplace_bf16(n + 3 * k + m, n, k)
     x = synth.f32_to_bf16_bits(np.random.default_rng(k + m).standard_normal((m, k)).astype(np.float32))
