@@ -182,9 +182,17 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode(const uint8_t* __restri
 // its 32 k values in registers for the whole row sweep; per row it expands
 // its codes to exact (unscaled) E2M1 values in bf16 and accumulates
 // v_dot2_f32_bf16 products, then applies the block scale with one fp32 FMA
-// (MXFP4: 2^e, exact; NVFP4: the E4M3 block scale, per 16).  Each lane ends
-// with one partial sum per (activation row, weight row); the 64 lanes x W
-// waves are summed through LDS in a fixed order.
+// (MXFP4: 2^e, exact; NVFP4: the E4M3 block scale, per 16).  MXFP4 with one
+// activation row instead folds the scale into the convert and takes the dot
+// products off the vector ALU onto the MFMA (the diagonal form below).  Each
+// lane ends with one partial sum per (activation row, weight row); the 64
+// lanes x W waves are summed through LDS in a fixed order.
+// MXFP4, one activation row: dot products on the MFMA diagonal (1) or with
+// v_dot2_f32_bf16 (0).  Interleaved A/B on 28672 x 8192: 23.35-24.15 against
+// 23.89-24.85 us, 63 of 63 parity cases on both.
+#ifndef MXQ_DV_MFMA1
+#define MXQ_DV_MFMA1 1
+#endif
 template <bool kNv, int M, int RB, int U, int W, bool kBf16Out>
 __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __restrict__ wq,
                                                               const uint8_t* __restrict__ ws,
@@ -192,6 +200,10 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
                                                               int64_t k, const uint16_t* __restrict__ x,
                                                               void* __restrict__ y) {
   static_assert(RB % U == 0, "rows per block must be a multiple of the unroll");
+  // MXFP4 at one activation row: dot products on the MFMA (see below)
+  constexpr bool kDiagMfma = !kNv && M == 1 && MXQ_DV_MFMA1;
+  const int de = threadIdx.x & 3;                                        // diagonal element
+  const bool ddiag = ((threadIdx.x & 15) >> 2) == ((threadIdx.x & 63) >> 4);  // lane holds one
   // per-wave partial sums: red[wave][act row][weight row][lane]
   __shared__ float red[W][M][RB][64];
   // Scale bytes of a wave's 8 rows for its 2048-k range (64 MXFP4 or 128
@@ -312,6 +324,36 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const unsigned d[4] = {codes[u].x, codes[u].y, codes[u].z, codes[u].w};
+        if constexpr (kDiagMfma) {
+          // MXFP4, one activation row: the lane's 32 codes are one block, so
+          // its scale rides in the convert (exact bf16, as in the ring), and
+          // the 16x16x32 MFMA of the lanes' weight fragments (A: lane (g, c)
+          // gives row c, k 8g..8g+7) with their activation fragments at the
+          // same k (B: column c) has on its diagonal D[c][c] the dot product
+          // of lanes c, 16 + c, 32 + c, 48 + c.  Off-diagonal entries pair
+          // different lanes' k and are dropped; lane (g, 4g + e) holds
+          // D[4g + e][4g + e] as element e.  One convert per two weights and
+          // four MFMAs replace the dot products and the scale multiply.
+          const float scale = e8m0_as_scale(sc[u] & 0xFFu);
+          f32x4 dm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
+            const bf16x8 wa = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            const bf16x8 xb = {xs[0][4 * j][0], xs[0][4 * j][1], xs[0][4 * j + 1][0], xs[0][4 * j + 1][1],
+                               xs[0][4 * j + 2][0], xs[0][4 * j + 2][1], xs[0][4 * j + 3][0], xs[0][4 * j + 3][1]};
+            dm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb, dm, 0, 0, 0);
+          }
+          float dv = dm[0];
+          dv = de == 1 ? dm[1] : dv;
+          dv = de == 2 ? dm[2] : dv;
+          dv = de == 3 ? dm[3] : dv;
+          red[wave][0][r0 + u][lane] += ddiag ? dv : 0.f;
+          continue;
+        }
         bf16x2 w[16];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
