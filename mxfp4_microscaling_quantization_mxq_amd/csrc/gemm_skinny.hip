@@ -112,6 +112,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
+  // activation copy a goes to wave a mod NW: up to 16 rows, a wave whose
+  // last slot has no real rows skips it and waits on one copy fewer (see the
+  // decode ring); taller tiles keep padding with a re-read (the branch costs
+  // them registers, 48 B of spill at 128 rows)
+  const bool xfull = MT > 16 || wave + NW * (XC - 1) < MT / G::XRPI;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = k / 32, kx = kFp8 ? k : k / 2;
@@ -184,7 +189,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
       bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
     if constexpr (!RS) bdma4(rws, offws, sc * G::ScB, sl.ws + 256 * wave);
 #pragma unroll
-    for (int j = 0; j < XC; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
+    for (int j = 0; j < XC; j++)
+      if (j < XC - 1 || xfull) bdma16(rx, offx[j], sc * G::XRowB, sl.x + dx[j]);
     if constexpr (!RS) {
 #pragma unroll
       for (int j = 0; j < XS; j++) bdma4(rxs, offxs[j], sc * G::ScB, sl.xs + dxs[j]);
@@ -250,8 +256,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   // meet the other waves, refill, multiply.
   auto step = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    constexpr int N = (NR - 2) * D;
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    constexpr int N = (NR - 2) * D, N1 = (NR - 2) * (D - 1);
+    if (xfull)
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((N1 & 15) | ((N1 >> 4) << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
     if (s < nst) compute(slot_tag, stage_of(s));
@@ -282,7 +291,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   if constexpr (RS) {
     // the scale loads are older than the NR - 1 stages of copies in flight;
     // the first stage's barrier publishes the activation scales
-    wait_vmcnt<(NR - 1) * D>();
+    if (xfull)
+      wait_vmcnt<(NR - 1) * D>();
+    else
+      wait_vmcnt<(NR - 1) * (D - 1)>();
 #pragma unroll
     for (int p = 0; p < PU; p++) {
       const int i = lane + 64 * p;
@@ -394,6 +406,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
+  // every wave pads its activation copies to the same count (skipping the
+  // pads as k_gemm_skinny does measured within 1 % either way here)
+  constexpr bool xfull = true;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = k / 32, kx = 2 * k;
@@ -520,8 +535,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   // multiply.
   auto step = [&](auto slot_tag, int s) {
     constexpr int B = decltype(slot_tag)::value;
-    constexpr int N = (NR - 2) * D;
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    constexpr int N = (NR - 2) * D, N1 = (NR - 2) * (D - 1);
+    if (xfull)
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((N1 & 15) | ((N1 >> 4) << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
     if (s < nst) {
@@ -552,7 +570,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   if constexpr (RS) {
     // older than the NR - 1 stages of copies in flight; only this wave
     // reads its rows' scales
-    wait_vmcnt<(NR - 1) * D>();
+    if (xfull)
+      wait_vmcnt<(NR - 1) * D>();
+    else
+      wait_vmcnt<(NR - 1) * (D - 1)>();
 #pragma unroll
     for (int p = 0; p < PU; p++) {
       const int i = lane + 64 * p;

@@ -919,6 +919,14 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 //     a 28672 x 8192 weight).  The k order of a block's sum changes with
 //     its rotation; the result is still one fixed order per output row.
 //   * NVFP4: the tensor scale multiplies the fp32 sums in the epilogue.
+// Short waves skip their padding activation copy (1) or re-read activation
+// rows into a scratch row so every wave issues the same count (0).
+// Interleaved A/B on 28672 x 8192, bitwise-equal results: m = 4 22.2-22.3
+// against 22.8-23.2 us, m = 16 24.0-24.1 against 25.1-26.0, m = 64
+// 51.8-52.4 against 55.8-56.2, NVFP4 m = 16 33.0 against 33.5.
+#ifndef MXQ_DD_XSKIP
+#define MXQ_DD_XSKIP 1
+#endif
 // Longest k whose scale rows the decode ring can keep resident in LDS.
 constexpr int kDdResK = 8192;
 // Stage geometry of the decode ring for KS k per stage (512 or 256).
@@ -969,11 +977,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   using Slot = DdSlot<MT, NW, KS, kNv, RS>;
   constexpr int RB = 16 * NW;                          // weight rows per block
   constexpr int MTT = (MT + 15) / 16;                  // 16-row activation tiles
-  constexpr int XPW = (MT / G::XRPI + NW - 1) / NW;    // activation copies per wave per stage
-  constexpr int D = G::WC + (RS ? 0 : G::SCP) + XPW;   // copies per wave per stage
+  constexpr int XPW = (MT / G::XRPI + NW - 1) / NW;    // activation copies per wave per stage, at most
+  constexpr int XC = MT / G::XRPI;                     // activation copies per stage (real rows)
+  constexpr int D = G::WC + (RS ? 0 : G::SCP) + XPW;   // copies per wave per stage, at most
   static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 8 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
+  // Activation copies are dealt round robin (copy a to wave a mod NW), so a
+  // wave issues XPW or XPW - 1 of them.  With MXQ_DD_XSKIP the short waves
+  // issue one copy fewer and wait on their own count (a wave-uniform branch
+  // picks the immediate); without it they pad with a re-read of activation
+  // rows into a scratch row.
+  const bool xfull = !MXQ_DD_XSKIP || wave + NW * (XPW - 1) < XC;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
@@ -1051,7 +1066,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     // copies' longer one (a copy-only probe of the m = 4 ring: 22.0 against
     // 22.7 us with them last; the kernel itself gains about 1 %)
 #pragma unroll
-    for (int j = 0; j < XPW; j++) bdma16(rx, offx[j], sc * G::XRowB, sl.x + xdst[j]);
+    for (int j = 0; j < XPW; j++)
+      if (j < XPW - 1 || xfull) bdma16(rx, offx[j], sc * G::XRowB, sl.x + xdst[j]);
 #pragma unroll
     for (int q = 0; q < G::WC; q++)
       bdma16_nt(rw, offw[q], sc * G::RowB, sl.w + (16 * wave + G::RPI * q) * G::RowB);
@@ -1131,8 +1147,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     constexpr int B = decltype(slot_tag)::value;
     // this wave's copies of stage s have landed and its reads of the slot
     // about to be refilled are complete (lgkmcnt(0)), then the barrier
-    constexpr int N = (NR - 2) * D;
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    constexpr int N = (NR - 2) * D, N1 = (NR - 2) * (D - 1);
+    if (xfull)
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((N1 & 15) | ((N1 >> 4) << 14) | (7 << 4) | (0 << 8));
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, (B + NR - 1) % NR>{}, s + NR - 1);
     if (s < nst) compute(slot_tag, stage_of(s));
@@ -1172,7 +1191,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   if constexpr (RS) {
     // the scale loads are older than the NR - 1 stages of copies in flight;
     // only this wave reads its rows' scales, so no barrier is needed
-    wait_vmcnt<(NR - 1) * D>();
+    if (xfull)
+      wait_vmcnt<(NR - 1) * D>();
+    else
+      wait_vmcnt<(NR - 1) * (D - 1)>();
 #pragma unroll
     for (int p = 0; p < PU; p++) {
       const int i = lane + 64 * p;
