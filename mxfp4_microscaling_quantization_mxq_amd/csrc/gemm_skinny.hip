@@ -94,6 +94,9 @@ __device__ __forceinline__ SkSlot<MT, NW, KS, kFp8, RS>& sk_slot() {
 // Longest k whose scale rows the ring keeps resident in LDS.
 constexpr int kSkResK = 8192;
 
+#ifndef MXQ_SK_WUNI
+#define MXQ_SK_WUNI 1
+#endif
 template <bool kFp8, int MT, int NW, int NR, int KS, bool RS, bool kBf16Out>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
@@ -110,7 +113,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_skinny(const uint8_t* __res
   constexpr int D = WC + (RS ? 0 : 1 + XS) + XC;     // copies per wave per stage
   constexpr int WSW = swz(G::U), XSW = swz(G::XU);   // swizzle periods
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: the branches on it stay scalar
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = MXQ_SK_WUNI ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   // activation copy a goes to wave a mod NW: up to 16 rows, a wave whose
   // last slot has no real rows skips it and waits on one copy fewer (see the
@@ -404,7 +409,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dynamic_skinny(const uint16_t* _
   constexpr int QPL = (NB + 64 * NW - 1) / (64 * NW); // blocks each lane quantizes
   constexpr int WSW = swz(G::U), TSW = swz(G::XU);
   static_assert(MT % 16 == 0 && NR >= 2 && NR <= 4 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform, as in k_gemm_skinny
   const int g = lane >> 4, col = lane & 15;
   // every wave pads its activation copies to the same count (skipping the
   // pads as k_gemm_skinny does measured within 1 % either way here)

@@ -212,7 +212,8 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_decode_valu(const uint8_t* __r
   // about 10 % of the MXFP4 decode time)
   constexpr int SB = kNv ? 128 : 64;  // scale bytes per row per range
   __shared__ __attribute__((aligned(16))) uint8_t sstage[W][8][SB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches and offsets
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int64_t kq = k / 2;                   // code bytes per row
   const int64_t ks = kNv ? k / 16 : k / 32;  // scale bytes per row
@@ -927,6 +928,12 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 #ifndef MXQ_DD_XSKIP
 #define MXQ_DD_XSKIP 1
 #endif
+// The wave index in a scalar register (1: readfirstlane) or as a vector
+// value (0).  Interleaved A/B: m = 16 23.8-24.1 against 24.0-24.9 us, m = 64
+// 51.0-51.2 against 51.9-52.2, NVFP4 m = 16 32.1 against 32.6, m = 4 even.
+#ifndef MXQ_DD_WUNI
+#define MXQ_DD_WUNI 1
+#endif
 // Longest k whose scale rows the decode ring can keep resident in LDS.
 constexpr int kDdResK = 8192;
 // Stage geometry of the decode ring for KS k per stage (512 or 256).
@@ -981,7 +988,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   constexpr int XC = MT / G::XRPI;                     // activation copies per stage (real rows)
   constexpr int D = G::WC + (RS ? 0 : G::SCP) + XPW;   // copies per wave per stage, at most
   static_assert((MT % 16 == 0 || MT < 16) && NR >= 2 && NR <= 8 && (NR - 2) * D < 64, "tile / ring depth / vmcnt range");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: held in a scalar register, so the branches
+  // on it (xfull) are scalar and its address terms stay off the VGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = MXQ_DD_WUNI ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   // Activation copies are dealt round robin (copy a to wave a mod NW), so a
   // wave issues XPW or XPW - 1 of them.  With MXQ_DD_XSKIP the short waves

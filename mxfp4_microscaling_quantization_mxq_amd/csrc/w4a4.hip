@@ -168,6 +168,9 @@ __device__ __forceinline__ uint8_t* w4_scales() {
 // per SIMD) or 8 (2 x 4 of 128 x 64, two waves per SIMD, so one wave's
 // MFMAs cover the other's waits).  BN = 128 halves the tile's columns (8
 // waves of 128 x 32): twice the tiles where 256 x 256 leaves CUs idle.
+#ifndef MXQ_W4A4_WUNI
+#define MXQ_W4A4_WUNI 1
+#endif
 template <int NWV, int OUT, int BN>
 __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void k_w4a4_ring(const uint8_t* __rest
   constexpr int CJ = RPW / 8;         // A copy instructions per wave
   constexpr int RPWB = BN / NWV;      // B rows each wave copies
   constexpr int CJB = RPWB / 8;       // B copy instructions per wave
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = MXQ_W4A4_WUNI ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;  // uniform
   const int wm = wave / WNC, wn = wave % WNC;
   const int half = lane >> 5, r32 = lane & 31;
 
