@@ -34,9 +34,11 @@ current stream):
      per-launch average is the kernel's steady-state duration.  The roofline
      figures (GB/s, TFLOP/s, fractions of the datasheet peak and of the
      measured ceiling) use it; both durations are in the JSON line.
-The on-box ceilings (a pure streaming read of the decode weight's size, the
-fp4 and bf16 MFMA issue rates with the shader clock they ran at) come from
-the measurement kernels in libmxq_ceiling.so.  After timing, the quality
+The on-box ceilings (a pure streaming read of the decode weight's size, a
+pure streaming write of the largest output, the fp4 and bf16 MFMA issue
+rates with the shader clock they ran at) come from the measurement kernels
+in libmxq_ceiling.so; an HBM op is held to the time the pure read of its
+read bytes plus the pure write of its written bytes would take.  After timing, the quality
 metrics (NMSE, cosine; host, float64) of the tiny reference and of the
 NVFP4-vs-MXFP4 tensors and products are computed from the GPU's outputs.
 The JSON line's value is the decode GEMV's achieved HBM bandwidth at m = 1.
@@ -155,11 +157,12 @@ def main():
         s1 = torch.empty((256, 16), dtype=u8, device=dev)
         y1 = torch.empty((256, 512), dtype=torch.float32, device=dev)
         g1 = torch.empty((1, 256), dtype=bf16, device=dev)
-        ops.append(("tiny_quantize_f32", lambda: mxq.quantize(w1d, q1, s1), quant_bytes(256, 512, 4), 0, "hbm"))
+        ops.append(("tiny_quantize_f32", lambda: mxq.quantize(w1d, q1, s1), quant_bytes(256, 512, 4), 0, "hbm",
+                    mx_bytes(256, 512)))
         ops.append(("tiny_dequantize_f32", lambda: mxq.dequantize(q1, s1, y=y1),
-                    mx_bytes(256, 512) + 256 * 512 * 4, 0, "hbm"))
+                    mx_bytes(256, 512) + 256 * 512 * 4, 0, "hbm", 256 * 512 * 4))
         ops.append(("tiny_gemv_m1", lambda: mxq.gemv_w4a16(q1, s1, x1d, y=g1), gemv_bytes(256, 512, 1),
-                    2 * 256 * 512, "hbm"))
+                    2 * 256 * 512, "hbm", 256 * 2))
         keep["tiny"] = (w1, x1, y1, g1)
     if "quant" in parts:
         x3 = to_dev(synth.dynamic_quantize())
@@ -167,11 +170,11 @@ def main():
         sets = [(x3 if c == 0 else x3.clone(), torch.empty((16384, 4096), dtype=u8, device=dev),
                  torch.empty((16384, 256), dtype=u8, device=dev)) for c in range(n3)]
         ops.append(("quantize_16384x8192_bf16", rotating(sets, lambda x, q, s: mxq.quantize(x, q, s)),
-                    quant_bytes(16384, 8192), 0, "hbm"))
+                    quant_bytes(16384, 8192), 0, "hbm", mx_bytes(16384, 8192)))
         # rotated MXFP4 (32-point block Hadamard fused ahead of the quantizer)
         ops.append(("quantize_hadamard32_16384x8192_bf16",
                     rotating(sets, lambda x, q, s: mxq.quantize_hadamard(x, 32, q, s)), quant_bytes(16384, 8192), 0,
-                    "hbm"))
+                    "hbm", mx_bytes(16384, 8192)))
         # TransFP4 blocks: tensor-scale pass + quantize pass (x read twice),
         # then the dequantization back to bf16
         ntf = 16384 * 8192
@@ -181,14 +184,14 @@ def main():
         tf4_bytes = ntf // 2 + ntf // 16 + ntf // 32 + ntf // 16  # codes, E4M3, meta, bf16 residual
         ops.append(("transfp4_quantize_16384x8192_bf16",
                     rotating(tsets, lambda x, q, s, m, r, g: mxq.transfp4_quantize(x, None, q, s, m, r, g)),
-                    2 * 2 * ntf + tf4_bytes, 0, "hbm"))
+                    2 * 2 * ntf + tf4_bytes, 0, "hbm", tf4_bytes))
         ydq = [torch.empty((16384, 8192), dtype=bf16, device=dev) for _ in tsets]
         for (x, q, s_, m, r, g) in tsets:
             mxq.transfp4_quantize(x, None, q, s_, m, r, g)
         ops.append(("transfp4_dequantize_16384x8192_bf16",
                     rotating([(q, s_, m, r, g, y) for (x, q, s_, m, r, g), y in zip(tsets, ydq)],
                              lambda q, s_, m, r, g, y: mxq.transfp4_dequantize(q, s_, m, r, g, y=y)),
-                    tf4_bytes + 2 * ntf, 0, "hbm"))
+                    tf4_bytes + 2 * ntf, 0, "hbm", 2 * ntf))
         # MXFP4 dequantize of the same tensor back to bf16 (codes and scales
         # of the plain quantize above)
         dsets = []
@@ -197,7 +200,7 @@ def main():
             mxq.quantize(x, q2, s2)
             dsets.append((q2, s2, y))
         ops.append(("dequantize_16384x8192_bf16", rotating(dsets, lambda q, s_, y: mxq.dequantize(q, s_, y=y)),
-                    ntf // 2 + ntf // 32 + 2 * ntf, 0, "hbm"))
+                    ntf // 2 + ntf // 32 + 2 * ntf, 0, "hbm", 2 * ntf))
     if "gemv" in parts:
         n2, k2 = 28672, 8192
         w2, _ = synth.decode_gemv(1)
@@ -211,7 +214,7 @@ def main():
             ym = torch.empty((m, n2), dtype=bf16, device=dev)
             ops.append((f"gemv_w4a16_m{m}",
                         rotating([(q, s, xm, ym) for q, s in copies], lambda q, s, x, y: mxq.gemv_w4a16(q, s, x, y=y)),
-                        gemv_bytes(n2, k2, m), 2 * m * n2 * k2, "hbm"))
+                        gemv_bytes(n2, k2, m), 2 * m * n2 * k2, "hbm", 2 * m * n2))
         # the same weight in NVFP4 (E4M3 per 16 + fp32 tensor scale)
         qn2, sn2, gn2 = mxq.nv_quantize(to_dev(w2))
         del w2
@@ -223,7 +226,7 @@ def main():
             ops.append((f"nv_gemv_w4a16_m{m}",
                         rotating([(q, s) for q, s in ncopies_nv],
                                  lambda q, s, x=xm, y=ym: mxq.nv_gemm(q, s, gn2, x, y=y)),
-                        nv_bytes(n2, k2) + m * k2 * 2 + m * n2 * 2, 2 * m * n2 * k2, "hbm"))
+                        nv_bytes(n2, k2) + m * k2 * 2 + m * n2 * 2, 2 * m * n2 * k2, "hbm", 2 * m * n2))
         # decode-sized W4A4 / W4A8 on the same weight (the small-m kernel:
         # the weight stream bounds it), and W4A4 straight from bf16
         # activations with their quantization fused into the GEMM
@@ -234,16 +237,16 @@ def main():
         out16 = 16 * n2 * 2
         ops.append(("decode_w4a4_m16", rotating([(q, s) for q, s in copies],
                                                 lambda q, s: mxq.gemm_w4a4(qx16, sx16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + mx_bytes(16, k2) + out16, 2 * 16 * n2 * k2, "hbm"))
+                    mx_bytes(n2, k2) + mx_bytes(16, k2) + out16, 2 * 16 * n2 * k2, "hbm", out16))
         ops.append(("decode_w4a8_m16", rotating([(q, s) for q, s in copies],
                                                 lambda q, s: mxq.gemm_w4a8(qx8, sx8, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2, "hbm"))
+                    mx_bytes(n2, k2) + 16 * k2 + 16 * k2 // 32 + out16, 2 * 16 * n2 * k2, "hbm", out16))
         ops.append(("decode_w4a4_dynamic_m16", rotating([(q, s) for q, s in copies],
                                                         lambda q, s: mxq.gemm_w4a4_dynamic(x16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm"))
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm", out16))
         ops.append(("decode_w4a8_dynamic_m16", rotating([(q, s) for q, s in copies],
                                                         lambda q, s: mxq.gemm_w4a8_dynamic(x16, q, s, c=y16)),
-                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm"))
+                    mx_bytes(n2, k2) + 16 * k2 * 2 + out16, 2 * 16 * n2 * k2, "hbm", out16))
     if "w4a4" in parts:
         a4, b4 = synth.w4a4_operands()
         a4d = to_dev(a4)
@@ -256,7 +259,7 @@ def main():
         sets = [(a4d if c == 0 else a4d.clone(), qa4 if c == 0 else torch.empty_like(qa4),
                  sa4 if c == 0 else torch.empty_like(sa4)) for c in range(na)]
         ops.append(("quantize_a_8192x8192_bf16", rotating(sets, lambda x, q, s: mxq.quantize(x, q, s)),
-                    quant_bytes(8192, 8192), 0, "hbm"))
+                    quant_bytes(8192, 8192), 0, "hbm", mx_bytes(8192, 8192)))
         # the GEMM is compute-bound (its 68 MB of operands may stay in the cache)
         ops.append(("gemm_w4a4_8192", lambda: mxq.gemm_w4a4(qa4, sa4, qb4, sb4, c=c4),
                     2 * mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3, "fp4"))
@@ -272,7 +275,7 @@ def main():
         sets8 = [(a4d if c == 0 else sets[c][0], qa8 if c == 0 else torch.empty_like(qa8),
                   sa8 if c == 0 else torch.empty_like(sa8)) for c in range(na)]
         ops.append(("quantize_fp8_a_8192x8192_bf16", rotating(sets8, lambda x, q, s: mxq.quantize_fp8(x, q, s)),
-                    8192 * 8192 * 3 + 8192 * 256, 0, "hbm"))
+                    8192 * 8192 * 3 + 8192 * 256, 0, "hbm", 8192 * 8192 + 8192 * 256))
         ops.append(("gemm_w4a8_8192", lambda: mxq.gemm_w4a8(qa8, sa8, qb4, sb4, c=c4),
                     8192 * 8192 + 8192 * 256 + mx_bytes(8192, 8192) + 8192 * 8192 * 2, 2 * 8192 ** 3, "fp8"))
     if "c5" in parts:
@@ -293,10 +296,12 @@ def main():
 
         def mxqz(x, q, s, g):
             mxq.quantize(x, q, s)
-        ops.append(("nv_quantize_w_8192x4096", rotating(nvw, nvq), n5 * k5 * 2 * 2 + nv_bytes(n5, k5), 0, "hbm"))
-        ops.append(("nv_quantize_x_4096x4096", rotating(nvx, nvq), m5 * k5 * 2 * 2 + nv_bytes(m5, k5), 0, "hbm"))
-        ops.append(("mx_quantize_w_8192x4096", rotating(mxw, mxqz), quant_bytes(n5, k5), 0, "hbm"))
-        ops.append(("mx_quantize_x_4096x4096", rotating(mxx, mxqz), quant_bytes(m5, k5), 0, "hbm"))
+        ops.append(("nv_quantize_w_8192x4096", rotating(nvw, nvq), n5 * k5 * 2 * 2 + nv_bytes(n5, k5), 0, "hbm",
+                    nv_bytes(n5, k5)))
+        ops.append(("nv_quantize_x_4096x4096", rotating(nvx, nvq), m5 * k5 * 2 * 2 + nv_bytes(m5, k5), 0, "hbm",
+                    nv_bytes(m5, k5)))
+        ops.append(("mx_quantize_w_8192x4096", rotating(mxw, mxqz), quant_bytes(n5, k5), 0, "hbm", mx_bytes(n5, k5)))
+        ops.append(("mx_quantize_x_4096x4096", rotating(mxx, mxqz), quant_bytes(m5, k5), 0, "hbm", mx_bytes(m5, k5)))
         y5n = torch.empty((m5, n5), dtype=bf16, device=dev)
         y5m = torch.empty((m5, n5), dtype=bf16, device=dev)
         _, wnq, wns, wng = nvw[0]
@@ -314,7 +319,7 @@ def main():
         csrc = torch.empty(1 << 30, dtype=u8, device=dev)
         cdst = torch.empty_like(csrc)
         csrc.fill_(1)
-        ops.append(("copy_1GiB", lambda: cdst.copy_(csrc), 2 << 30, 0, "hbm"))
+        ops.append(("copy_1GiB", lambda: cdst.copy_(csrc), 2 << 30, 0, "hbm", 1 << 30))
     if args.ops:
         pref = tuple(args.ops.split(","))
         ops = [o for o in ops if o[0].startswith(pref)]
@@ -325,8 +330,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run_step():
-        for _, fn, _, _, _ in ops:
-            fn()
+        for op in ops:
+            op[1]()
 
     for _ in range(args.warmup):
         run_step()
@@ -341,7 +346,11 @@ def main():
 
     # 2 and 3: per op, single launches and bursts
     per_op = {}
-    for name, fn, nbytes, flops, bound in ops:
+    for op in ops:
+        # (name, fn, bytes, flops, bound[, bytes written]): an HBM op's bytes
+        # count reads and writes; the written part prices its ceiling
+        name, fn, nbytes, flops, bound = op[:5]
+        wbytes = op[5] if len(op) > 5 else 0
         fn()
         fn()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -370,6 +379,7 @@ def main():
             "GB/s": round(nbytes / ms / 1e6, 1),
             "TFLOP/s": round(flops / ms / 1e9, 1) if flops else None,
             "bytes": nbytes,
+            "bytes_written": wbytes,
             "flops": flops,
             "bound": bound,
         }
@@ -395,6 +405,13 @@ def main():
         if ceil:
             c = ceil.get({"hbm": "hbm_read_GBps", "fp4": "mfma_fp4_TFLOPs", "fp8": "mfma_fp8_TFLOPs",
                           "bf16": "mfma_bf16_TFLOPs"}[bound])
+            sm = ceil.get("hbm_stream_model")
+            if c and bound == "hbm" and sm:
+                # the streaming model's time for the op's read and written
+                # bytes: t0 + read / BW_read + written / BW_write
+                w = r["bytes_written"]
+                t_us = sm["t0_us"] + (r["bytes"] - w) / sm["read_GBps"] / 1e3 + w / sm["write_GBps"] / 1e3
+                c = round(r["bytes"] / t_us / 1e3, 1)
             if c:
                 out["ceiling"] = c
                 out["frac_of_ceiling"] = round(a / c, 4)
@@ -447,6 +464,15 @@ def measure_ceilings(torch, dev, stream):
       algorithmic bytes) per launch, rotating over copies that defeat the
       256 MB cache, burst-timed like the library's ops; hbm_read_1GiB_GBps
       the same for 1 GiB per launch;
+    - hbm_write_GBps: a pure streaming write (one pass, 16-byte stores with
+      the streaming hint, best of 1-8 stores per lane) of 268,435,456 bytes
+      per launch, the largest output an op writes (16384 x 8192 bf16), and
+      of 67,108,864 bytes;
+    - hbm_stream_model: t = t0 + read bytes / BW_read + written bytes /
+      BW_write, with t0 and BW_read fitted to the two read sizes and
+      BW_write to the two write sizes.  An HBM op's ceiling is its bytes over
+      that time for its own read and written bytes (for the m = 1 GEMV, all
+      reads of the fitted size, it is hbm_read_GBps);
     - mfma_fp4_TFLOPs / mfma_bf16_TFLOPs: back-to-back 32x32 MFMAs on random
       register operands on every SIMD (8 waves per CU), with the shader clock
       read in the kernel (core-cycle counter over the constant-rate counter);
@@ -457,6 +483,7 @@ def measure_ceilings(torch, dev, stream):
     lib = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.mxqc_stream_read.argtypes = [P, I64, I, I, P, P]
+    lib.mxqc_stream_write.argtypes = [P, I64, I, P]
     lib.mxqc_mfma_fp4.argtypes = [P, I64, I, P, P, P]
     lib.mxqc_mfma_bf16.argtypes = [P, I64, I, P, P, P]
     sptr = ctypes.c_void_p(stream.cuda_stream)
@@ -500,6 +527,38 @@ def measure_ceilings(torch, dev, stream):
         out[label.replace("_GBps", "_shape")] = {"loads_in_flight": best[1], "blocks": best[2],
                                                  "us": round(best[3] * 1e3, 2)}
         del buf
+    wt = {}
+    for nbytes in (67_108_864, 268_435_456):
+        ncp = max(2, -(-COLD_BYTES // nbytes))
+        buf = torch.empty(ncp * nbytes, dtype=torch.uint8, device=dev)
+        best = None
+        for unroll in (1, 2, 4, 8):
+            st = {"i": 0}
+
+            def fn(unroll=unroll):
+                off = (st["i"] % ncp) * nbytes
+                st["i"] += 1
+                rc = lib.mxqc_stream_write(ctypes.c_void_p(buf.data_ptr() + off), nbytes, unroll, sptr)
+                assert rc == 0, rc
+            ms = timed(fn)
+            if best is None or ms < best[1]:
+                best = (unroll, ms)
+        wt[nbytes] = best
+        del buf
+    out["hbm_write_GBps"] = round(268_435_456 / wt[268_435_456][1] / 1e6, 1)
+    out["hbm_write_shape"] = {"bytes": 268_435_456, "stores_per_lane": wt[268_435_456][0],
+                              "us": round(wt[268_435_456][1] * 1e3, 2),
+                              "us_at_67108864_bytes": round(wt[67_108_864][1] * 1e3, 2)}
+    # streaming model t = t0 + read bytes / BW_read + written bytes / BW_write,
+    # fitted to the two read sizes (t0, BW_read) and the two write sizes
+    # (BW_write); GB/s and microseconds
+    r0, r1 = out["hbm_read_shape"]["us"], out["hbm_read_1GiB_shape"]["us"]
+    w0, w1 = wt[67_108_864][1] * 1e3, wt[268_435_456][1] * 1e3
+    if r1 > r0 and w1 > w0:  # else the rows keep the plain read ceiling
+        bwr = ((1 << 30) - 124_854_272) / (r1 - r0) / 1e3
+        bww = (268_435_456 - 67_108_864) / (w1 - w0) / 1e3
+        out["hbm_stream_model"] = {"t0_us": round(r0 - 124_854_272 / bwr / 1e3, 2), "read_GBps": round(bwr, 1),
+                                   "write_GBps": round(bww, 1)}
     src = torch.randint(0, 256, (8192,), dtype=torch.uint8, device=dev)
     wall_khz = lib.mxqc_wall_clock_khz()
     out["peak_sclk_MHz"] = lib.mxqc_peak_clock_khz() / 1e3

@@ -4,6 +4,9 @@
 //
 //   mxqc_stream_read   pure streaming read of a byte range (the HBM ceiling a
 //                      weight-streaming kernel of the same size can reach)
+//   mxqc_stream_write  pure streaming write of a byte range, 16-byte stores
+//                      with the streaming hint (the ceiling for the bytes a
+//                      dequantizer or quantizer writes)
 //   mxqc_mfma_fp4      back-to-back V_MFMA_SCALE_F32_32X32X64_F8F6F4 with two
 //                      E2M1 operands on registers (the fp4 MFMA issue ceiling)
 //   mxqc_mfma_bf16     back-to-back V_MFMA_F32_32X32X16_BF16 (the bf16 one)
@@ -39,6 +42,20 @@ __global__ __launch_bounds__(256) void k_stream_read(const i32x4* __restrict__ p
   }
   // the xor is kept alive by a store no input makes true in practice
   if (acc == 0x7F3A5C11) sink[blockIdx.x] = (float)acc;
+}
+
+// One pass over the range: lane t of a block writes U 16-byte units, 256
+// units apart (the layout of the library's chunked streaming kernels), with
+// the streaming hint.  The stored pattern depends on the index.
+template <int U>
+__global__ __launch_bounds__(256) void k_stream_write(i32x4* __restrict__ p, int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int64_t i = base + (int64_t)u * 256;
+    const int v = (int)i;
+    if (i < n16) __builtin_nontemporal_store((i32x4){v, v ^ 0x5A5A5A5A, v + 1, ~v}, p + i);
+  }
 }
 
 struct Clocks {
@@ -140,6 +157,23 @@ __attribute__((visibility("default"))) int mxqc_stream_read(const void* p, int64
     hipLaunchKernelGGL(k_stream_read<16>, dim3(blocks), dim3(256), 0, st, (const i32x4*)p, n16, sink);
   else
     hipLaunchKernelGGL(k_stream_read<8>, dim3(blocks), dim3(256), 0, st, (const i32x4*)p, n16, sink);
+  return (int)hipGetLastError();
+}
+
+// Writes bytes (a multiple of 16, 16-byte aligned) of device memory at p in
+// one pass, `unroll` (1, 2, 4 or 8) stores per lane.  Returns a hipError_t
+// code.
+__attribute__((visibility("default"))) int mxqc_stream_write(void* p, int64_t bytes, int unroll, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)((n16 + 256 * unroll - 1) / (256 * unroll));
+  if (unroll == 1)
+    hipLaunchKernelGGL(k_stream_write<1>, dim3(grid), dim3(256), 0, st, (i32x4*)p, n16);
+  else if (unroll == 2)
+    hipLaunchKernelGGL(k_stream_write<2>, dim3(grid), dim3(256), 0, st, (i32x4*)p, n16);
+  else if (unroll == 8)
+    hipLaunchKernelGGL(k_stream_write<8>, dim3(grid), dim3(256), 0, st, (i32x4*)p, n16);
+  else
+    hipLaunchKernelGGL(k_stream_write<4>, dim3(grid), dim3(256), 0, st, (i32x4*)p, n16);
   return (int)hipGetLastError();
 }
 
