@@ -686,7 +686,18 @@ __device__ __forceinline__ void tf4_candidate(const float (&v)[8], float amax, f
 // Pass 1: per block of this grid, the largest |y'| (residual-free rotated
 // values) of its grid-stride share, as fp32 bits, into part[block]; then
 // k_nv_scale folds the partials into s_t = amax' / 2688.
-constexpr int kTf4U = 4;  // lane slots per thread per step (loads in flight)
+// Lane slots per thread per step (loads in flight).  The grid is at most
+// kScaleMaxParts = 2048 blocks of 4 waves, 8 waves per SIMD on 256 CUs: it
+// fits the chip in one round only if the kernel stays within 64 VGPRs.
+// 4 slots took 67 (7 waves per SIMD, so 256 blocks ran as a second round):
+// TransFP4 quantize of 16384 x 8192 bf16, interleaved A/B, 238.1 us with 4
+// slots, 227.7 with 3 (38 VGPRs), 225.9 with 2 (24 VGPRs); the next step's
+// loads issued before the current step's arithmetic measured the same
+// (225.4-228.0 us with 1-3 slots).
+#ifndef MXQ_TF4A_U
+#define MXQ_TF4A_U 2
+#endif
+constexpr int kTf4U = MXQ_TF4A_U;
 
 template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_tf4_amax(const u32x4* __restrict__ x, int64_t nlanes,
