@@ -934,6 +934,22 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 #ifndef MXQ_DD_WUNI
 #define MXQ_DD_WUNI 1
 #endif
+// NVFP4 with up to 4 activation rows: E4M3 block scales applied to the
+// 16-k sums of 4x4x4 block MFMAs (1) or to every weight element before the
+// 16x16x32 MFMA (0).
+#ifndef MXQ_DD_NVB
+#define MXQ_DD_NVB 1
+#endif
+// NVFP4 with 5..8 activation rows and resident scales: the 4x4x4 form on two
+// row quads (256-k stages, 4 slots) (1), or the 16-row ring (0).
+#ifndef MXQ_DD_NVB8
+#define MXQ_DD_NVB8 1
+#endif
+// The same 4x4x4 form for MXFP4 at up to 4 activation rows (1), or the
+// 16x16x32 MFMA with 12 zero activation rows (0).
+#ifndef MXQ_DD_MXB
+#define MXQ_DD_MXB 0
+#endif
 // Longest k whose scale rows the decode ring can keep resident in LDS.
 constexpr int kDdResK = 8192;
 // Stage geometry of the decode ring for KS k per stage (512 or 256).
@@ -1088,9 +1104,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
     }
   };
 
-  f32x4 acc[MTT];
+  // Up to 4 (MXFP4) or 8 (NVFP4) activation rows: 4x4x4 block MFMAs
+  // (acc[q] holds activation rows 4q..4q+3 of the lane's weight row, over
+  // its lane group's chunks); otherwise 16x16x32 MFMAs on pre-scaled
+  // weights
+  constexpr bool kB4 = kNv ? (MT == 4 || MT == 8) && MXQ_DD_NVB : MT == 4 && MXQ_DD_MXB;
+  constexpr int NQ = MT / 4;  // activation row quads of the 4x4x4 form
+  constexpr int NACC = kB4 ? NQ : MTT;
+  f32x4 acc[NACC];
 #pragma unroll
-  for (int t = 0; t < MTT; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NACC; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int wrow = 16 * wave + col;  // this lane's block weight row
   auto compute = [&](auto slot_tag, unsigned sc) {
     constexpr int B = decltype(slot_tag)::value;
@@ -1120,6 +1143,69 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
         const u32x4 sv = *(const u32x4*)(sl.s + (G::SCP * wave + h) * 256 + 16 * col);
         svs[4 * h] = sv.x; svs[4 * h + 1] = sv.y; svs[4 * h + 2] = sv.z; svs[4 * h + 3] = sv.w;
       }
+    }
+    if constexpr (kB4) {
+      // Up to 4 activation rows: 4x4x4 block MFMAs.  Lane (col, g) is MFMA
+      // block 4g + col / 4, column col % 4: its weight row's 32 k of chunk
+      // 4i + g in bf16 (exact), against activation row col % 4 at the same
+      // k, so the lane's D column is its own weight row.  MXFP4: the E8M0
+      // scale rides in the convert.  NVFP4: the codes are converted
+      // unscaled and each 16-k block's sum takes its row's E4M3 scale in 4
+      // FMAs (instead of a multiply per weight element).
+      const uint8_t* xb[NQ];
+      int xsw[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; q++) {
+        const int xr = 4 * q + (col & 3);
+        xb[q] = sl.x + (xr < m ? xr : MT) * G::XRowB;
+        xsw[q] = xr < m ? (xr & 15) : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < G::STEPS; i++) {
+        const u32x4 cw = *(const u32x4*)(sl.w + wrow * G::RowB + (((4 * i + g) ^ (col % G::U)) << 4));
+        unsigned sb2;
+        if constexpr (kNv && RS)
+          sb2 = *(const uint16_t*)(sp + 8 * i + 2 * g);
+        else if constexpr (kNv)
+          sb2 = (svs[2 * i + (g >> 1)] >> (16 * (g & 1))) & 0xFFFFu;
+        else
+          sb2 = (svs[i] >> (8 * g)) & 0xFFu;
+        const float cs = kNv ? 1.0f : e8m0_as_scale(sb2);
+        const unsigned d[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {  // the chunk's two 16-k halves (NVFP4 blocks)
+          f32x4 db[NQ];
+#pragma unroll
+          for (int q = 0; q < NQ; q++) db[q] = kNv ? (f32x4){0.f, 0.f, 0.f, 0.f} : acc[q];
+#pragma unroll
+          for (int jj = 0; jj < 2; jj++) {
+            const int j = 2 * h + jj;  // k 8j .. 8j + 7 of the chunk
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], cs, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], cs, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], cs, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], cs, 3);
+#pragma unroll
+            for (int q = 0; q < NQ; q++) {
+              const bf16x8 xa = *(const bf16x8*)(xb[q] + ((16 * i + ((4 * g + j) ^ xsw[q])) << 4));
+              db[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k((bf16x4){xa[0], xa[1], xa[2], xa[3]},
+                                                             (bf16x4){p0[0], p0[1], p1[0], p1[1]}, db[q], 0, 0, 0);
+              db[q] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k((bf16x4){xa[4], xa[5], xa[6], xa[7]},
+                                                             (bf16x4){p2[0], p2[1], p3[0], p3[1]}, db[q], 0, 0, 0);
+            }
+          }
+          if constexpr (kNv) {
+            const float sbk = h ? e4m3_value_b<1>(sb2) : e4m3_value_b<0>(sb2);
+#pragma unroll
+            for (int q = 0; q < NQ; q++)
+#pragma unroll
+              for (int e = 0; e < 4; e++) acc[q][e] = __builtin_fmaf(sbk, db[q][e], acc[q][e]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < NQ; q++) acc[q] = db[q];
+          }
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int i = 0; i < G::STEPS; i++) {
@@ -1224,9 +1310,31 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   }
   wait_vmcnt<0>();
 
-  // lane holds y[16t + 4g + i][n0 + wrow]
   const float st = kNv ? *gscale : 1.0f;
   const int64_t nn = n0 + wrow;
+  if constexpr (kB4) {
+    // sum the four lane groups' k shares (the same order in every lane),
+    // then lane group g writes activation rows 4q + g
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        acc[q][e] += __shfl_xor(acc[q][e], 16);
+        acc[q][e] += __shfl_xor(acc[q][e], 32);
+      }
+      const float v = g == 0 ? acc[q][0] : g == 1 ? acc[q][1] : g == 2 ? acc[q][2] : acc[q][3];
+      const int64_t mm = 4 * q + g;
+      if (nn < n && mm < m) {
+        const float o = v * st;
+        if (kBf16Out)
+          ((uint16_t*)y)[mm * n + nn] = f32_to_bf16_rne(o);
+        else
+          ((float*)y)[mm * n + nn] = o;
+      }
+    }
+    return;
+  }
+  // lane holds y[16t + 4g + i][n0 + wrow]
   if (nn < n) {
 #pragma unroll
     for (int t = 0; t < MTT; t++)
@@ -1302,6 +1410,8 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
   if (m <= 16 && res) {
     if (m <= 4)
       launch_decode_dma<kNv, 4, 7, MXQ_DD_RS4, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+    else if (kNv && MXQ_DD_NVB8 && m <= 8)
+      launch_decode_dma<kNv, 8, 7, 4, 256, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
     else if constexpr (kNv)
       launch_decode_dma<kNv, 16, 7, MXQ_DD_RS16_NV, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
     else
@@ -1320,6 +1430,9 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
     launch_decode_dma<kNv, 64, 7, 3, 256>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
 }
 
+#ifndef MXQ_DD_NVMIN
+#define MXQ_DD_NVMIN 2
+#endif
 #ifndef MXQ_DD_MAXM
 #define MXQ_DD_MAXM 64
 #endif
@@ -1341,7 +1454,7 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
     return launch_w4a16(nv, wq, ws, gscale, n, k, (const uint16_t*)x + MXQ_DD_MAXM * k, m - MXQ_DD_MAXM,
                         (uint8_t*)y + MXQ_DD_MAXM * n * (bf16_out ? 2 : 4), bf16_out, st);
   }
-  if (ring && m >= (nv ? 4 : 2) && m <= MXQ_DD_MAXM) {
+  if (ring && m >= (nv ? MXQ_DD_NVMIN : 2) && m <= MXQ_DD_MAXM) {
     nv ? launch_decode_ring<true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
        : launch_decode_ring<false>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (!nv && m >= 5 && m <= 16) {

@@ -469,13 +469,13 @@ constexpr int kRingWaves = MXQ_W4A4_RING_WAVES;
 #define MXQ_W4A4_NARROW_BELOW 129
 #endif
 
+// Returns the launch status (the skinny launcher reads, and so clears, the
+// error state itself; its status is passed on as is).
 template <int OUT>
-static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
-                            int64_t n, int64_t k, void* c, uint8_t* cs, hipStream_t st) {
-  if (OUT != kOutMx && gemm_skinny_applies(m, k)) {
-    launch_w4a4_skinny(aq, as, bq, bs, m, n, k, c, OUT == kOutBf16, st);
-    return;
-  }
+static hipError_t launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                                  int64_t m, int64_t n, int64_t k, void* c, uint8_t* cs, hipStream_t st) {
+  if (OUT != kOutMx && gemm_skinny_applies(m, k))
+    return launch_w4a4_skinny(aq, as, bq, bs, m, n, k, c, OUT == kOutBf16, st);
   // the ring addresses its row panels with 32-bit offsets: 256 rows * k/2
   // bytes stay below 2^31 for k < 2^24
   if (k % 1024 == 0 && k >= 1024 && k < (1 << 24)) {
@@ -486,31 +486,28 @@ static void launch_w4a4_out(const uint8_t* aq, const uint8_t* as, const uint8_t*
       if (tm_n * ((n + 255) / 256) < MXQ_W4A4_NARROW_BELOW) {
         const unsigned tiles = (unsigned)(tm_n * ((n + 127) / 128));
         hipLaunchKernelGGL((k_w4a4_ring<8, OUT, 128>), dim3(tiles), dim3(512), 0, st, aq, as, bq, bs, m, n, k, c, cs);
-        return;
+        return hipGetLastError();
       }
     }
     const unsigned tiles = (unsigned)(tm_n * ((n + 255) / 256));
     hipLaunchKernelGGL((k_w4a4_ring<kRingWaves, OUT, 256>), dim3(tiles), dim3(64 * kRingWaves), 0, st, aq, as, bq,
                        bs, m, n, k, c, cs);
-    return;
+    return hipGetLastError();
   }
   dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
   hipLaunchKernelGGL(k_w4a4_direct<OUT>, grid, dim3(256), 0, st, aq, as, bq, bs, m, n, k, c, cs);
+  return hipGetLastError();
 }
 
 hipError_t launch_w4a4(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                        int64_t n, int64_t k, void* c, bool bf16_out, hipStream_t st) {
-  if (bf16_out)
-    launch_w4a4_out<kOutBf16>(aq, as, bq, bs, m, n, k, c, nullptr, st);
-  else
-    launch_w4a4_out<kOutF32>(aq, as, bq, bs, m, n, k, c, nullptr, st);
-  return hipGetLastError();
+  return bf16_out ? launch_w4a4_out<kOutBf16>(aq, as, bq, bs, m, n, k, c, nullptr, st)
+                  : launch_w4a4_out<kOutF32>(aq, as, bq, bs, m, n, k, c, nullptr, st);
 }
 
 hipError_t launch_w4a4_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t m,
                           int64_t n, int64_t k, uint8_t* cq, uint8_t* cs, hipStream_t st) {
-  launch_w4a4_out<kOutMx>(aq, as, bq, bs, m, n, k, cq, cs, st);
-  return hipGetLastError();
+  return launch_w4a4_out<kOutMx>(aq, as, bq, bs, m, n, k, cq, cs, st);
 }
 
 }  // namespace mxq

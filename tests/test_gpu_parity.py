@@ -765,13 +765,15 @@ def test_nv_gemm_ragged():
             check_product(y, yref, S, dt == torch.bfloat16, f"nv gemm n={n} k={k} m={m}")
 
 
-# NVFP4 weights at decode sizes: the staged-scale path of the m <= 4 kernel
+# NVFP4 weights at decode sizes: the staged-scale path of the m <= 3 kernel
 # (k % 256 == 0, whole 2048-k ranges; a partial last range and k % 32 == 16
-# take the byte-wise path), and the m = 4..64 ring kernel (n >= 14336,
-# k % 512 == 0; 512-k stages up to 4 rows, 256-k stages above; two passes
-# for m = 65..128) with ragged weight rows.
+# take the byte-wise path), and the m = 2..64 ring kernel (n >= 14336,
+# k % 512 == 0; 512-k stages up to 4 rows, 256-k stages above; block scales
+# applied after 4x4x4 block MFMAs up to 4 rows, and up to 8 rows when k <=
+# 8192; two passes for m = 65..128) with ragged weight rows.
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 2304, 3), (77, 4112, 2), (14373, 1536, 2),
-                                   (14373, 512, 4), (14400, 2048, 5), (14373, 1024, 16), (14373, 512, 17),
+                                   (14400, 8192, 3), (14373, 512, 4), (14400, 2048, 5), (14447, 4096, 6),
+                                   (14373, 7680, 8), (14336, 8704, 7), (14373, 1024, 16), (14373, 512, 17),
                                    (14400, 1536, 32), (14336, 2560, 40), (14447, 1024, 64),
                                    (14373, 512, 66), (14400, 1024, 128), (14336, 8704, 4), (14373, 9216, 9),
                                    (14447, 8192, 13), (14400, 7680, 4)])
@@ -794,9 +796,9 @@ def decode_weight_nv():
     return oracle.nv_quantize(w)
 
 
-@pytest.mark.parametrize("m", [1, 4, 16, 32, 64, 100])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32, 64, 100])
 def test_nv_decode_full_size_sampled(m):
-    """The 28672 x 8192 decode weight in NVFP4 at m = 1, 4, 16, 32, 64, 100."""
+    """The 28672 x 8192 decode weight in NVFP4 at m = 1, 2, 4, 8, 16, 32, 64, 100."""
     qo, so, go = decode_weight_nv()
     _, x = synth.decode_gemv(m)
     n = qo.shape[0]
