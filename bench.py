@@ -220,7 +220,7 @@ def main():
         del w2
         ncn = ncopies(nv_bytes(n2, k2))
         ncopies_nv = [(qn2, sn2)] + [(qn2.clone(), sn2.clone()) for _ in range(ncn - 1)]
-        for m in (1, 16, 64):
+        for m in (1, 4, 16, 64):
             xm = to_dev(synth.decode_gemv(m)[1])
             ym = torch.empty((m, n2), dtype=bf16, device=dev)
             ops.append((f"nv_gemv_w4a16_m{m}",

@@ -925,6 +925,9 @@ static void launch_decode(const uint8_t* wq, const uint8_t* ws, const float* gsc
 // Interleaved A/B on 28672 x 8192, bitwise-equal results: m = 4 22.2-22.3
 // against 22.8-23.2 us, m = 16 24.0-24.1 against 25.1-26.0, m = 64
 // 51.8-52.4 against 55.8-56.2, NVFP4 m = 16 33.0 against 33.5.
+#ifndef MXQ_DD_XNEED
+#define MXQ_DD_XNEED 1
+#endif
 #ifndef MXQ_DD_XSKIP
 #define MXQ_DD_XSKIP 1
 #endif
@@ -1013,7 +1016,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
   // issue one copy fewer and wait on their own count (a wave-uniform branch
   // picks the immediate); without it they pad with a re-read of activation
   // rows into a scratch row.
-  const bool xfull = !MXQ_DD_XSKIP || wave + NW * (XPW - 1) < XC;
+  // Where a wave issues at most one activation copy per stage, the copies of
+  // rows at or past m are skipped as well (those rows read the zero row):
+  // at m = 1, one copy per stage instead of MT / XRPI.
+  const int xc_need = XPW == 1 && MXQ_DD_XNEED ? (int)min((int64_t)XC, (m + G::XRPI - 1) / G::XRPI) : XC;
+  const bool xfull = !MXQ_DD_XSKIP || wave + NW * (XPW - 1) < xc_need;
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int rows_w = (int)min((int64_t)RB, n - n0);
   const int64_t kq = k / 2, ks = kNv ? k / 16 : k / 32, kx = k * 2;
@@ -1430,6 +1437,14 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
     launch_decode_dma<kNv, 64, 7, 3, 256>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
 }
 
+// Fewest activation rows that take the decode ring: MXFP4 from 1 (the ring
+// measured 21.5-21.7 against 22.6-23.1 us for the vector-ALU kernel at m = 1
+// on 28672 x 8192, interleaved A/B, with the activation copies of rows past
+// m skipped), NVFP4 from 2 (at m = 1 the vector-ALU kernel, which applies
+// each E4M3 scale once per 16 products, measured even with the ring).
+#ifndef MXQ_DD_MXMIN
+#define MXQ_DD_MXMIN 1
+#endif
 #ifndef MXQ_DD_NVMIN
 #define MXQ_DD_NVMIN 2
 #endif
@@ -1439,10 +1454,8 @@ static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float
 
 hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n,
                         int64_t k, const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
-  // The decode ring from m = 2 (MXFP4) or m = 4 (NVFP4): the NVFP4 dequant
-  // costs vector-ALU work per weight element in the ring, while the
-  // vector-ALU kernel applies each E4M3 scale once per 16 products (measured
-  // on 28672 x 8192: m = 2 29.5 vs 40-45 us, m = 4 47-50 vs 39-41 us).
+  // The decode ring from m = MXQ_DD_MXMIN (MXFP4) or MXQ_DD_NVMIN (NVFP4)
+  // activation rows, for weights of at least 14336 rows and k % 512 == 0.
   const bool ring = k % 512 == 0 && k <= (1 << 24) && n >= 16 * 7 * 128;
   // m = MAXM+1 .. 2 MAXM in two passes, the first over MAXM activation rows
   // on the ring, the second over the rest by this same dispatch: two reads of
@@ -1454,7 +1467,7 @@ hipError_t launch_w4a16(bool nv, const uint8_t* wq, const uint8_t* ws, const flo
     return launch_w4a16(nv, wq, ws, gscale, n, k, (const uint16_t*)x + MXQ_DD_MAXM * k, m - MXQ_DD_MAXM,
                         (uint8_t*)y + MXQ_DD_MAXM * n * (bf16_out ? 2 : 4), bf16_out, st);
   }
-  if (ring && m >= (nv ? MXQ_DD_NVMIN : 2) && m <= MXQ_DD_MAXM) {
+  if (ring && m >= (nv ? MXQ_DD_NVMIN : MXQ_DD_MXMIN) && m <= MXQ_DD_MAXM) {
     nv ? launch_decode_ring<true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st)
        : launch_decode_ring<false>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
   } else if (!nv && m >= 5 && m <= 16) {

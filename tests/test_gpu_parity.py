@@ -661,7 +661,8 @@ def test_gemv_ragged_shapes(n, k, m):
     mx_w4a16_case(w, x, f"w4a16 n={n} k={k} m={m}")
 
 
-# The vector-ALU decode kernel (m <= 4) on ragged row counts and k.
+# The vector-ALU decode kernel (m <= 4; MXFP4 only where the ring does not
+# apply: n < 14336 or k % 512 != 0) on ragged row counts and k.
 # Blocks of 8 (m = 1) or 16 (m = 2..4) rows with one k range per wave
 # (6144 < k <= 8192, k % 256 == 0) stage their scale bytes block-wide; the
 # last, partial block and other k take the per-wave path.
@@ -676,14 +677,16 @@ def test_gemv_m1_shapes(n, k, m):
 
 
 # Shapes that reach the DMA-fed decode kernel (n >= 14336 rows, k a
-# multiple of 512, 2 <= m <= 64): up to 16 rows with resident scale rows
+# multiple of 512, 1 <= m <= 64; activation copies of rows past m skipped in
+# the 4-row tile): up to 16 rows with resident scale rows
 # (k <= 8192: 512-k stages for 4-row tiles, 256-k stages for 16-row tiles)
 # and with per-stage scale copies (k > 8192), two to sixteen 256-k stages
 # against a four-slot ring (32-row tiles) and a three-slot ring (64-row
 # tiles), row tails that leave part of the last block empty, and activation
 # counts on both sides of every tile height; m = 65..128 runs as a 64-row pass
 # plus a pass over the rest.
-@pytest.mark.parametrize("n,k,m", [(14336, 512, 2), (14373, 1024, 3), (14447, 1536, 4), (14400, 2048, 5),
+@pytest.mark.parametrize("n,k,m", [(14336, 512, 1), (14373, 7680, 1), (14400, 8704, 1), (14336, 512, 2),
+                                   (14373, 1024, 3), (14447, 1536, 4), (14400, 2048, 5),
                                    (14336, 2560, 16), (15000, 1536, 12), (14336, 4096, 2), (14336, 512, 17),
                                    (14373, 1536, 32), (14400, 4096, 33), (14447, 1024, 48), (14336, 2560, 64),
                                    (15000, 512, 64), (14336, 1024, 65), (14373, 1536, 100), (14400, 512, 128),
@@ -694,8 +697,8 @@ def test_gemv_decode_dma_shapes(n, k, m):
     mx_w4a16_case(w, x, f"w4a16 dma n={n} k={k} m={m}")
 
 
-@pytest.mark.parametrize("n,k,m", [(70, 256, 1), (33, 4096, 3), (14336, 512, 4), (14336, 1024, 16), (40, 320, 7),
-                                   (64, 512, 130)])
+@pytest.mark.parametrize("n,k,m", [(70, 256, 1), (14336, 1024, 1), (33, 4096, 3), (14336, 512, 4), (14336, 1024, 16),
+                                   (40, 320, 7), (64, 512, 130)])
 def test_gemv_scale_code_zero_blocks(n, k, m):
     """Blocks with E8M0 code 0 (2^-127) and non-zero elements: what the
     quantizer emits for a block whose largest magnitude is below 2^-125.
