@@ -1407,6 +1407,13 @@ static void launch_decode_dma(const uint8_t* wq, const uint8_t* ws, const float*
 #ifndef MXQ_DD_RS16
 #define MXQ_DD_RS16 4, 256
 #endif
+// MXFP4 at m = 1 on a 1-row activation tile with NR 512-k slots (which
+// LDS then holds up to 4 of) instead of the 4-row, 3-slot ring (0).
+// Interleaved A/B on 28672 x 8192: NR = 3 21.41 against 21.68 us (within
+// the run-to-run spread), NR = 4 22.94; not used.
+#ifndef MXQ_DD_M1NR
+#define MXQ_DD_M1NR 0
+#endif
 #ifndef MXQ_DD_RS16_NV
 #define MXQ_DD_RS16_NV 4, 256
 #endif
@@ -1414,6 +1421,12 @@ template <bool kNv>
 static void launch_decode_ring(const uint8_t* wq, const uint8_t* ws, const float* gscale, int64_t n, int64_t k,
                                const void* x, int64_t m, void* y, bool bf16_out, hipStream_t st) {
   const bool res = MXQ_DD_RS && k <= kDdResK;
+  if constexpr (!kNv && MXQ_DD_M1NR > 0) {
+    if (m == 1 && res) {
+      launch_decode_dma<false, 1, 7, MXQ_DD_M1NR, 512, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
+      return;
+    }
+  }
   if (m <= 16 && res) {
     if (m <= 4)
       launch_decode_dma<kNv, 4, 7, MXQ_DD_RS4, true>(wq, ws, gscale, n, k, x, m, y, bf16_out, st);
