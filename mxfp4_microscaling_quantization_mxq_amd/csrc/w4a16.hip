@@ -1152,10 +1152,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_w4a16_decode_dma(const uint8_t* 
       }
     }
     if constexpr (kB4) {
-      // Up to 4 activation rows: 4x4x4 block MFMAs.  Lane (col, g) is MFMA
-      // block 4g + col / 4, column col % 4: its weight row's 32 k of chunk
-      // 4i + g in bf16 (exact), against activation row col % 4 at the same
-      // k, so the lane's D column is its own weight row.  MXFP4: the E8M0
+      // Up to 4 (MXFP4) or 8 (NVFP4) activation rows, in quads of 4: 4x4x4
+      // block MFMAs.  Lane (col, g) is MFMA block 4g + col / 4, column
+      // col % 4: its weight row's 32 k of chunk 4i + g in bf16 (exact),
+      // against activation row 4q + col % 4 at the same k for quad q, so
+      // the lane's D column is its own weight row.  MXFP4: the E8M0
       // scale rides in the convert.  NVFP4: the codes are converted
       // unscaled and each 16-k block's sum takes its row's E4M3 scale in 4
       // FMAs (instead of a multiply per weight element).
