@@ -1161,15 +1161,16 @@ def test_w4a4_quant_full_size():
 
 # Long k (2^20 = 1,048,576, 2048 stages of 512): the products' 32-bit copy
 # offsets, k rotations and stage loops far from the small test shapes.  The
-# W4A16 decode ring needs n >= 14336 weight rows, so its case takes k = 2^17
-# (1024 stages of 256 k, about 1 GB of codes).
+# W4A16 decode ring needs n >= 14336 weight rows, so its cases take k = 2^17
+# (1024 stages of 256 k at 64 rows, 256 stages of 512 k at one row; about
+# 1 GB of codes).
 # Random codes and scales stand in for quantized tensors (host memory stays
 # small); outputs are checked on sampled rows and columns.
 @pytest.mark.parametrize("kind,m,n,k", [("w4a4", 16, 130, 1 << 20), ("w4a4", 260, 300, 1 << 20),
                                         ("w4a4", 40, 70, (1 << 20) + 32), ("w4a8", 16, 130, 1 << 20),
                                         ("w4a8", 260, 300, 1 << 20), ("w4a8", 40, 70, (1 << 20) + 32),
                                         ("gemv", 1, 7, 1 << 20), ("gemv", 3, 300, 1 << 20),
-                                        ("gemv", 64, 14373, 1 << 17),
+                                        ("gemv", 64, 14373, 1 << 17), ("gemv", 1, 14373, 1 << 17),
                                         ("dyn", 16, 130, 1 << 20), ("dyn8", 16, 130, 1 << 20)])
 def test_products_long_k(kind, m, n, k):
     rng = np.random.default_rng(m + n + k)
