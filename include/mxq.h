@@ -277,9 +277,13 @@ MXQ_API mxq_status nvq_dequantize(const uint8_t *q, const uint8_t *s,
 /*
  * W4A16 product with an NVFP4 weight, software two-level dequantization:
  * y[m][n] = s_t * sum_k x[m][k] * (E4M3(ws[n][k/16]) * E2M1(wq[n][k])),
- * with the block-scaled codes formed exactly in bf16 in registers, bf16
- * MFMA with fp32 accumulation, and the tensor scale *wgscale applied once in
- * the epilogue.  x[m][k] bf16; y written as ydt.  k % 16 == 0.
+ * bf16 MFMA with fp32 accumulation and the tensor scale *wgscale applied
+ * once in the epilogue.  The block scale is applied either to the codes
+ * (s_b * q formed exactly in bf16 in registers) or, for up to 8 activation
+ * rows on weights of at least 14336 rows, to each 16-k block's fp32 sum of
+ * the exact unscaled products (one fp32 multiply-add per block and output);
+ * either way the result is held to the same bound against the exact sum.
+ * x[m][k] bf16; y written as ydt.  k % 16 == 0.
  * [infra-guide sec. 4.1: x_hat = s_tensor * s_block * q; TransFP4 page
  * sec. 2.5: scales are decoded at matrix load, no 16-bit copy of W.]
  */
